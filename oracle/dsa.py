@@ -1,0 +1,231 @@
+"""fp64 CPU oracle of the DeepSeek Sparse Attention (DSA) forward path.
+
+Test infrastructure: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It is a plain, slow, step-by-step
+restatement of the method; it shares no code with the HIP path and never runs
+in the product path.
+
+The method, as the DeepSeek-V3.2 write-up on intelliparadigm.com describes it
+("DSA", sections 2.1-3.1):
+  * a lightning indexer scores every query token against every earlier token
+    with I[t,s] = ReLU(q_t . W_index . k_s) on 128-dim index vectors held in
+    FP8 (section 2.2);
+  * a fine-grained selection keeps, per query, the k = 2048 keys with the
+    highest index score (section 2.3);
+  * ordinary softmax attention then runs over the selected keys only, with all
+    query heads sharing one key/value head, MLA's MQA mode (sections 2.3, 3.1).
+
+Readings of points the pages leave open (each is a stated choice):
+  R1  W is folded into the index query before the FP8 product:
+      qf_t = dq(q8_t) @ W  (q a row vector, qf_j = sum_i q_i W_ij), then qf_t
+      is re-quantised to e4m3 with a per-row scale amax/448 (fp32, RNE);
+      amax = 0 gives scale 1.  The folded, re-quantised query is the FP8
+      operand of the score product.  The fp32 workload skips the re-quantising.
+  R2  keys of query t are s in [0, t] (its own token included), so a query
+      keeps m_t = min(k, t+1) keys.
+  R3  ties are broken by the lower key index; ReLU maps every u <= 0
+      (including -0.0) to +0.0, so zero scores tie.
+  R4  the selected set is reported in ascending key order, padded with -1.
+  R5  V of the shared latent row is its first Dv entries unless a separate V
+      is given.
+  R6  -0.0 re-quantises to the +0 code.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+
+IDX_DIM = 128
+
+
+# ---------------------------------------------------------------- inputs ---
+
+def dequant_rows(codes, scale) -> np.ndarray:
+    """dq(x8)[t, j] = e4m3(x8[t, j]) * scale[t], exact in fp64."""
+    return codecs.e4m3_decode(codes) * np.asarray(scale, dtype=np.float32).astype(np.float64)[:, None]
+
+
+def as_f64(x) -> np.ndarray:
+    """fp32 / bf16(uint16 bits) / fp64 arrays -> fp64."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return codecs.bf16_decode(x)
+    return x.astype(np.float64)
+
+
+# ------------------------------------------------------ R1: fold, requant ---
+
+def fold(q_rows: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """qf = q @ W in fp64, q as row vectors (section 2.2's q_t . W_index)."""
+    return np.asarray(q_rows, np.float64) @ np.asarray(w, np.float64)
+
+
+def requant(qf: np.ndarray):
+    """Per-row e4m3 re-quantisation of the folded query (reading R1).
+
+    scale_t = fp32(amax_t / 448), 1 when amax_t = 0;
+    code[t, j] = e4m3_RNE_sat(qf[t, j] / scale_t), quotient in fp64.
+    """
+    amax = np.max(np.abs(qf), axis=1)
+    scale = codecs.f64_to_f32_rne(np.where(amax > 0, amax / codecs.E4M3_MAX, 1.0))
+    codes = codecs.e4m3_encode(qf / scale.astype(np.float64)[:, None])
+    return codes, scale
+
+
+# ----------------------------------------------------- section 2.2: I[t,s] ---
+
+def relu(u: np.ndarray) -> np.ndarray:
+    """ReLU with +0.0 for every u <= 0 (reading R3)."""
+    return np.where(u > 0, u, 0.0)
+
+
+def index_scores_row(q_vals: np.ndarray, q_scale: float, k_vals: np.ndarray, k_scale, t: int) -> np.ndarray:
+    """I[t, s] for s in [0, t], fp64 (one row, causal).
+
+    u[s] = q_scale * k_scale[s] * sum_j q_vals[j] * k_vals[s, j];  I = ReLU(u).
+    For FP8 operands q_vals / k_vals are the decoded e4m3 values (their
+    128-term dot product is exact in fp64) and the scales are the per-row
+    fp32 scales; for fp32 operands the scales are 1.
+    """
+    dots = np.asarray(k_vals[: t + 1], np.float64) @ np.asarray(q_vals, np.float64)
+    ks = np.ones(t + 1) if k_scale is None else np.asarray(k_scale[: t + 1], np.float64)
+    u = float(q_scale) * (ks * dots)
+    return relu(u)
+
+
+def index_scores(q_vals, q_scale, k_vals, k_scale, pos) -> np.ndarray:
+    """Dense score matrix [T, S] with -inf where s > pos[t] (small inputs only)."""
+    T, S = q_vals.shape[0], k_vals.shape[0]
+    out = np.full((T, S), -np.inf)
+    for t in range(T):
+        p = min(int(pos[t]), S - 1)
+        qs = 1.0 if q_scale is None else float(q_scale[t])
+        out[t, : p + 1] = index_scores_row(q_vals[t], qs, k_vals, k_scale, p)
+    return out
+
+
+# ----------------------------------------------------- section 2.3: top-k ---
+
+def topk_row(scores: np.ndarray, k: int) -> np.ndarray:
+    """The min(k, n) best keys of one row under (higher score, then lower
+    index), returned in ascending key order (readings R3, R4).  Full sort."""
+    scores = np.asarray(scores, np.float64)
+    n = scores.shape[0]
+    m = min(k, n)
+    order = np.lexsort((np.arange(n), -scores))   # primary: -score, secondary: index
+    return np.sort(order[:m])
+
+
+def pad_idx(sel: np.ndarray, k: int) -> np.ndarray:
+    out = np.full(k, -1, dtype=np.int32)
+    out[: sel.shape[0]] = sel
+    return out
+
+
+# ------------------------------------------- sections 2.3 / 3.1: attention ---
+
+def attend(q_heads: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float):
+    """Softmax attention of H query heads over n shared key/value rows, fp64.
+
+    z[h, s] = scale * q_h . k_s;  p = softmax_s(z);  o_h = sum_s p[h, s] v_s.
+    Returns (o [H, Dv], lse [H]) with lse the natural-log normaliser of z.
+    """
+    q = np.asarray(q_heads, np.float64)
+    z = scale * (q @ np.asarray(k_rows, np.float64).T)
+    zmax = np.max(z, axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    den = np.sum(e, axis=1, keepdims=True)
+    o = (e / den) @ np.asarray(v_rows, np.float64)
+    return o, (zmax + np.log(den))[:, 0]
+
+
+# ---------------------------------------------------------- whole forward ---
+
+class PrefillOracle:
+    """One causal prefill (queries = keys = L tokens).
+
+    Arguments are host numpy arrays in the library's storage formats:
+      q_idx, k_idx : uint8 e4m3 codes [L,128] with fp32 scales [L]   (FP8)
+                     or float32 [L,128] with scales None              (fp32)
+      w            : uint16 bf16 bits or float32 [128,128]
+      q            : [L,H,Dk] (uint16 bf16 bits or float32)
+      kv           : [L,Dk]; v : [L,Dv] or None (then V = kv[:, :Dv])
+    """
+
+    def __init__(self, q_idx, q_scale, k_idx, k_scale, w, q, kv, v, topk, scale, Dv):
+        self.fp8 = q_scale is not None
+        if self.fp8:
+            qv = dequant_rows(q_idx, q_scale)
+            self.k_vals = codecs.e4m3_decode(k_idx)
+            self.k_scale = np.asarray(k_scale, np.float32).astype(np.float64)
+        else:
+            qv = as_f64(q_idx)
+            self.k_vals = as_f64(k_idx)
+            self.k_scale = None
+        self.qf = fold(qv, as_f64(w))
+        if self.fp8:
+            self.qf8, self.qf_scale = requant(self.qf)
+            self.q_vals = codecs.e4m3_decode(self.qf8)
+        else:
+            self.qf8, self.qf_scale = None, None
+            self.q_vals = self.qf
+        self.q, self.kv, self.v = q, kv, v
+        self.k, self.scale, self.Dv = topk, scale, Dv
+        self._kv64 = None
+
+    def _kv_rows(self):
+        if self._kv64 is None:
+            kv = as_f64(self.kv)
+            vv = as_f64(self.v) if self.v is not None else kv[:, : self.Dv]
+            self._kv64 = (kv, vv)
+        return self._kv64
+
+    def q_scale_of(self, t: int) -> float:
+        return 1.0 if self.qf_scale is None else float(self.qf_scale[t])
+
+    def scores_row(self, t: int) -> np.ndarray:
+        return index_scores_row(self.q_vals[t], self.q_scale_of(t), self.k_vals, self.k_scale, t)
+
+    def select_row(self, t: int) -> np.ndarray:
+        return topk_row(self.scores_row(t), self.k)
+
+    def attend_row(self, t: int, sel: np.ndarray):
+        kv, vv = self._kv_rows()
+        qh = as_f64(self.q[t])
+        return attend(qh, kv[sel], vv[sel], self.scale)
+
+    def row(self, t: int):
+        sel = self.select_row(t)
+        o, lse = self.attend_row(t, sel)
+        return pad_idx(sel, self.k), o, lse
+
+
+class DecodeOracle:
+    """One batched decode step: sequence b owns cache rows
+    [off[b], off[b+1]) and its query sits at position n_b - 1 over keys
+    [0, n_b) of its own cache."""
+
+    def __init__(self, q_idx, q_scale, k_idx, k_scale, w, q, kv, v, offsets, topk, scale, Dv):
+        qv = dequant_rows(q_idx, q_scale)
+        self.k_vals = codecs.e4m3_decode(k_idx)
+        self.k_scale = np.asarray(k_scale, np.float32).astype(np.float64)
+        self.qf = fold(qv, as_f64(w))
+        self.qf8, self.qf_scale = requant(self.qf)
+        self.q_vals = codecs.e4m3_decode(self.qf8)
+        self.q, self.kv, self.v = q, kv, v
+        self.off = np.asarray(offsets, np.int64)
+        self.k, self.scale, self.Dv = topk, scale, Dv
+
+    def scores_seq(self, b: int) -> np.ndarray:
+        lo, hi = int(self.off[b]), int(self.off[b + 1])
+        return index_scores_row(self.q_vals[b], float(self.qf_scale[b]), self.k_vals[lo:hi],
+                                self.k_scale[lo:hi], hi - lo - 1)
+
+    def seq(self, b: int):
+        lo, hi = int(self.off[b]), int(self.off[b + 1])
+        sel = topk_row(self.scores_seq(b), self.k)
+        kv = as_f64(self.kv[lo:hi][sel])
+        vv = as_f64(self.v[lo:hi][sel]) if self.v is not None else kv[:, : self.Dv]
+        o, lse = attend(as_f64(self.q[b]), kv, vv, self.scale)
+        return pad_idx(sel, self.k), o, lse
