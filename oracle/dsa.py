@@ -172,14 +172,6 @@ class PrefillOracle:
             self.q_vals = self.qf
         self.q, self.kv, self.v = q, kv, v
         self.k, self.scale, self.Dv = topk, scale, Dv
-        self._kv64 = None
-
-    def _kv_rows(self):
-        if self._kv64 is None:
-            kv = as_f64(self.kv)
-            vv = as_f64(self.v) if self.v is not None else kv[:, : self.Dv]
-            self._kv64 = (kv, vv)
-        return self._kv64
 
     def q_scale_of(self, t: int) -> float:
         return 1.0 if self.qf_scale is None else float(self.qf_scale[t])
@@ -191,9 +183,9 @@ class PrefillOracle:
         return topk_row(self.scores_row(t), self.k)
 
     def attend_row(self, t: int, sel: np.ndarray):
-        kv, vv = self._kv_rows()
-        qh = as_f64(self.q[t])
-        return attend(qh, kv[sel], vv[sel], self.scale)
+        k_rows = as_f64(self.kv[sel])
+        v_rows = as_f64(self.v[sel]) if self.v is not None else k_rows[:, : self.Dv]
+        return attend(as_f64(self.q[t]), k_rows, v_rows, self.scale)
 
     def row(self, t: int):
         sel = self.select_row(t)
@@ -208,8 +200,7 @@ class DecodeOracle:
 
     def __init__(self, q_idx, q_scale, k_idx, k_scale, w, q, kv, v, offsets, topk, scale, Dv):
         qv = dequant_rows(q_idx, q_scale)
-        self.k_vals = codecs.e4m3_decode(k_idx)
-        self.k_scale = np.asarray(k_scale, np.float32).astype(np.float64)
+        self.k_idx, self.k_scale = k_idx, k_scale
         self.qf = fold(qv, as_f64(w))
         self.qf8, self.qf_scale = requant(self.qf)
         self.q_vals = codecs.e4m3_decode(self.qf8)
@@ -219,8 +210,9 @@ class DecodeOracle:
 
     def scores_seq(self, b: int) -> np.ndarray:
         lo, hi = int(self.off[b]), int(self.off[b + 1])
-        return index_scores_row(self.q_vals[b], float(self.qf_scale[b]), self.k_vals[lo:hi],
-                                self.k_scale[lo:hi], hi - lo - 1)
+        k_vals = codecs.e4m3_decode(self.k_idx[lo:hi])
+        k_scale = np.asarray(self.k_scale[lo:hi], np.float32).astype(np.float64)
+        return index_scores_row(self.q_vals[b], float(self.qf_scale[b]), k_vals, k_scale, hi - lo - 1)
 
     def seq(self, b: int):
         lo, hi = int(self.off[b]), int(self.off[b + 1])

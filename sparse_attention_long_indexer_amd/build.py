@@ -1,0 +1,67 @@
+"""Build libdsa.so (HIP kernels + C ABI) for gfx950, in-tree.
+
+    python -m sparse_attention_long_indexer_amd.build
+
+Every source is compiled by hipcc for --offload-arch=gfx950 only, with packed
+fp32 instructions disabled, then linked into one shared library next to this
+file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdsa.so")
+
+SOURCES = ["fold.hip", "index_scores.hip", "topk.hip", "attn.hip", "api.cpp"]
+ARCH = "gfx950"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    for c in ("/opt/rocm/bin/hipcc", "hipcc"):
+        if os.path.isabs(c) and os.path.exists(c):
+            return c
+    return "hipcc"
+
+
+def _compile(src: str, obj: str) -> None:
+    lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
+    cmd = [hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libdsa.so; returns its path."""
+    with tempfile.TemporaryDirectory(prefix="dsa_build_") as tmp:
+        objs = [os.path.join(tmp, s.replace(".", "_") + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+            list(ex.map(_compile, SOURCES, objs))
+        out_tmp = LIB + ".tmp"
+        cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", out_tmp] + objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(out_tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

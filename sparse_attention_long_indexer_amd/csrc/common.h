@@ -1,0 +1,122 @@
+// Device helpers shared by the DSA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+constexpr int kIdxDim = 128;
+constexpr int kWave = 64;
+
+// ---- number formats ------------------------------------------------------
+
+// OCP e4m3fn code -> float (exact): E=0 subnormal M*2^-9, else (8+M)*2^(E-10).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = (e == 0) ? ldexpf((float)m, -9) : ldexpf((float)(8u + m), (int)e - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// double -> e4m3fn code, round to nearest (ties to even mantissa), saturating
+// at 448; zero (either sign) encodes as +0.  The grid step for |x| in
+// [2^e, 2^(e+1)) is 2^(e-3) (e >= -6), 2^-9 below 2^-6; scaling by a power of
+// two is exact, so rint() performs the only rounding.
+__device__ __forceinline__ uint32_t f64_to_e4m3_rne_sat(double x) {
+  const uint32_t sign = signbit(x) ? 0x80u : 0u;
+  double a = fabs(x);
+  if (!(a > 0.0)) return 0u;
+  if (a >= 448.0) return sign | 0x7Eu;
+  int ex;
+  frexp(a, &ex);                       // a = f * 2^ex, f in [0.5, 1)
+  int e = ex - 1;
+  if (e < -6) e = -6;
+  double n = rint(ldexp(a, 3 - e));    // grid steps, exact scaling
+  if (n == 0.0) return 0u;
+  double v = ldexp(n, e - 3);          // rounded magnitude (<= 448)
+  int ev;
+  frexp(v, &ev);
+  ev -= 1;
+  uint32_t code;
+  if (ev < -6) {
+    code = (uint32_t)ldexp(v, 9);                        // subnormal mantissa
+  } else {
+    code = ((uint32_t)(ev + 7) << 3) | ((uint32_t)ldexp(v, 3 - ev) - 8u);
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even (inputs are finite here)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+// Order-preserving map of a float score to uint32 (larger score -> larger
+// key); -0.0 is folded onto +0.0 so that zeros tie.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- MFMA wrappers ------------------------------------------------------
+
+// 16x16x128 e4m3 x e4m3 -> fp32 (both operand formats code 0 = FP8 E4M3,
+// no block scaling).  Lane l supplies 32 bytes of row / column (l % 16);
+// lane group l / 16 selects the quarter of the 128-wide reduction; the
+// result lane l holds rows 4*(l/16) .. +3 of column l % 16.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 16x16x32 bf16 -> fp32; lane l supplies 8 values of row / column (l % 16)
+// for reduction slice l / 16; result layout as above.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8s& a, const v8s& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16((v8bf)a, (v8bf)b, c, 0, 0, 0);
+}
+
+// ---- wave helpers --------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// number of set bits of `mask` below this lane
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace dsa

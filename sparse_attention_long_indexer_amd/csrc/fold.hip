@@ -1,0 +1,93 @@
+// Fold W_index into the index query and re-quantise it to e4m3.
+//
+// The indexer score is q_t . W_index . k_s (DeepSeek-V3.2 write-up, section
+// 2.2).  Folding W into q once per query turns the per-pair work into one
+// 128-wide FP8 dot product; the folded row is re-quantised with its own
+// amax/448 scale so that the pair product stays FP8.
+//
+// Work: T x 128 x 128 MACs in fp64 (bit-reproducible codes), ~1/1024 of the
+// indexer's pair work.  One thread owns one output column j and keeps column
+// j of W in registers; a block walks kRows query rows held in LDS as fp64.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+
+constexpr int kFoldRows = 32;
+
+template <bool kFp8In, bool kWBf16>
+__global__ __launch_bounds__(128) void fold_kernel(const void* __restrict__ q_in,
+                                                   const float* __restrict__ q_scale,
+                                                   const void* __restrict__ w_in, int64_t T,
+                                                   void* __restrict__ q_out,
+                                                   float* __restrict__ s_out) {
+  __shared__ double qrow[kFoldRows][kIdxDim];
+  __shared__ double wmax[2][kFoldRows];
+  const int j = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kFoldRows;
+  const int nr = (int)min<int64_t>(kFoldRows, T - r0);
+
+  float wcol[kIdxDim];
+#pragma unroll
+  for (int i = 0; i < kIdxDim; ++i) {
+    if (kWBf16)
+      wcol[i] = bf16_to_f32(((const uint16_t*)w_in)[i * kIdxDim + j]);
+    else
+      wcol[i] = ((const float*)w_in)[i * kIdxDim + j];
+  }
+  for (int r = nr; r < kFoldRows; ++r) qrow[r][j] = 0.0;
+  for (int r = 0; r < nr; ++r) {
+    const int64_t t = r0 + r;
+    double v;
+    if (kFp8In)
+      v = (double)e4m3_to_f32(((const uint8_t*)q_in)[t * kIdxDim + j]) * (double)q_scale[t];
+    else
+      v = (double)((const float*)q_in)[t * kIdxDim + j];
+    qrow[r][j] = v;
+  }
+  __syncthreads();
+
+  double acc[kFoldRows];
+#pragma unroll
+  for (int r = 0; r < kFoldRows; ++r) acc[r] = 0.0;
+  for (int i = 0; i < kIdxDim; ++i) {
+    const double w = (double)wcol[i];
+#pragma unroll
+    for (int r = 0; r < kFoldRows; ++r) acc[r] = fma(qrow[r][i], w, acc[r]);
+  }
+
+  if (!kFp8In) {
+    for (int r = 0; r < nr; ++r) ((float*)q_out)[(r0 + r) * kIdxDim + j] = (float)acc[r];
+    return;
+  }
+  // per-row amax over the 128 columns (two waves)
+  const int wv = j >> 6;
+#pragma unroll
+  for (int r = 0; r < kFoldRows; ++r) {
+    double m = wave_max(fabs(acc[r]));
+    if ((j & 63) == 0) wmax[wv][r] = m;
+  }
+  __syncthreads();
+  for (int r = 0; r < nr; ++r) {
+    const double amax = max(wmax[0][r], wmax[1][r]);
+    const float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+    const uint32_t code = f64_to_e4m3_rne_sat(acc[r] / (double)s);
+    ((uint8_t*)q_out)[(r0 + r) * kIdxDim + j] = (uint8_t)code;
+    if (j == 0) s_out[r0 + r] = s;
+  }
+}
+
+hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, const void* w,
+                       bool w_bf16, int64_t T, void* q_out, float* s_out, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  dim3 grid((unsigned)((T + kFoldRows - 1) / kFoldRows));
+  if (fp8_in && w_bf16)
+    fold_kernel<true, true><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+  else if (fp8_in)
+    fold_kernel<true, false><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+  else
+    fold_kernel<false, false><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

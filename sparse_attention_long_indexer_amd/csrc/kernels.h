@@ -1,0 +1,57 @@
+// Launchers of the DSA kernels (internal to the library; the public
+// interface is include/dsa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// fold.hip
+hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, const void* w,
+                       bool w_bf16, int64_t T, void* q_out, float* s_out, hipStream_t st);
+
+// index_scores.hip: materialised scores for rows [row_begin, row_end)
+hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, const float* ks,
+                               bool fp8, int64_t T, int64_t S, const int64_t* q_pos,
+                               int64_t row_begin, int64_t row_end, float* out, int64_t ld,
+                               hipStream_t st);
+// decode: scores of query b over its own cache rows, written at key offsets
+hipError_t launch_index_scores_decode(const uint8_t* qf, const float* qs, const uint8_t* k,
+                                      const float* ks, const int64_t* offsets, int64_t B,
+                                      int64_t max_len, float* out, hipStream_t st);
+
+// topk.hip: rows are described by (row_off, n) pairs computed on device
+struct TopkRows {
+  const float* scores;
+  int64_t ld;                 // row stride when row_off == nullptr
+  const int64_t* row_off;     // optional per-row start offset into scores
+  const int64_t* q_pos;       // optional per-row position (n = min(S, pos+1))
+  int64_t S;                  // keys available (prefill) when seq_len == nullptr
+  const int64_t* seq_offsets; // decode: n_b = off[b+1]-off[b], start = off[b]
+  int64_t row_begin;          // first row (for q_pos lookup / output row)
+};
+size_t topk_workspace_bytes(int64_t rows, int64_t max_n, int64_t k);
+hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k, int32_t* idx_out,
+                       int32_t* count_out, void* ws, hipStream_t st);
+
+// attn.hip
+struct AttnArgs {
+  const void* q;        // [T][H][Dk]
+  const void* kv;       // [*][ld_kv]
+  const void* v;        // [*][ld_v] or nullptr
+  int64_t ld_kv, ld_v;
+  const int32_t* idx;   // [T][k]
+  const int64_t* seq_offsets;  // decode: query t reads cache rows [off[t], off[t+1])
+  int64_t S;            // rows of kv/v (prefill)
+  int64_t T, H, Dk, Dv, k;
+  float scale;
+  void* out;            // [T][H][Dv]
+  float* lse;           // [T][H] or nullptr
+};
+bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv);
+size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t k);
+hipError_t launch_attn(const AttnArgs& a, bool f32, void* ws, size_t ws_bytes, hipStream_t st);
+
+}  // namespace dsa

@@ -183,3 +183,39 @@ def make_decode(spec: DecodeSpec, seed: int = 0, device="cpu", lengths: Optional
     kv = _randn((total, spec.Dk), _gen(dev, spec.wid, seed, _T_K), dev, std, torch.bfloat16)
     return dict(q_idx=q_idx, q_scale=q_scale, k_idx=k_idx, k_scale=k_scale, w=w, q=q, kv=kv, v=None,
                 lengths=n, offsets=offsets.to(dev))
+
+
+# ---- stage-level inputs (each stage can be fed on its own) ----------------
+
+def make_scores(T: int, S: int, seed: int = 0, device="cpu", q_pos: Optional[torch.Tensor] = None,
+                levels: int = 64) -> torch.Tensor:
+    """fp32 score rows shaped like lightning-indexer output: about half exact
+    zeros (some stored as -0.0), positive values quantised to `levels` steps so
+    that exact ties are common, and -inf past each row's causal position."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 7_777 + 31)
+    x = torch.randn((T, S), generator=g, dtype=torch.float32)
+    x = torch.clamp(torch.round(x * (levels / 4.0)) / (levels / 4.0), min=0.0)
+    negz = torch.rand((T, S), generator=g) < 0.1
+    x = torch.where((x == 0) & negz, torch.full_like(x, -0.0), x)
+    if q_pos is None:
+        q_pos = torch.arange(T, dtype=torch.int64)
+    s = torch.arange(S)[None, :]
+    x = torch.where(s <= q_pos.cpu()[:, None], x, torch.full_like(x, float("-inf")))
+    return x.to(device)
+
+
+def make_selection(T: int, S: int, k: int, seed: int = 0, device="cpu", min_valid: int = 0) -> torch.Tensor:
+    """int32 [T][k] rows of ascending distinct key indices in [0, S), each row
+    holding a random number (>= min_valid) of valid entries followed by -1."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 9_973 + 17)
+    out = torch.full((T, k), -1, dtype=torch.int32)
+    cap = min(k, S)
+    for t in range(T):
+        m = int(torch.randint(min(min_valid, cap), cap + 1, (1,), generator=g))
+        if t == 0:
+            m = cap
+        sel = torch.randperm(S, generator=g)[:m].sort().values
+        out[t, :m] = sel.to(torch.int32)
+    return out.to(device)

@@ -1,0 +1,274 @@
+"""GPU parity of every stage and of the whole forward pass against the fp64
+oracle, through the C ABI.  Same seeded inputs on both sides; rules in
+tests/parity.py."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.dsa as od
+import parity as P
+from helpers import to_np
+from sparse_attention_long_indexer_amd import binding as B
+from sparse_attention_long_indexer_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()  # fails loudly when the library is missing
+    return torch.device("cuda:0")
+
+
+class RowsOf:
+    """Row accessor over a device tensor (copies one row at a time)."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, i):
+        return to_np(self.t[i])
+
+
+def oracle_prefill(spec, x):
+    return od.PrefillOracle(to_np(x["q_idx"]), to_np(x["q_scale"]), to_np(x["k_idx"]), to_np(x["k_scale"]),
+                            to_np(x["w"]), RowsOf(x["q"]), to_np(x["kv"]), to_np(x["v"]), spec.topk,
+                            spec.scale, spec.Dv)
+
+
+def sample_rows(L, k, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, 2, L - 1, L - 2, min(L - 1, k - 1), min(L - 1, k), min(L - 1, k + 1), min(L - 1, 2 * k)}
+    rows |= set(rng.integers(0, L, n).tolist())
+    return sorted(r for r in rows if 0 <= r < L)
+
+
+SMALL_H16 = gen.PREFILL_8K.with_(name="ragged_L777_h16", L=777, topk=128)
+SMALL_MLA = gen.PREFILL_32K.with_(name="ragged_L1000_mla", L=1000, topk=256)
+UNIT_MLA = gen.PREFILL_32K.with_(name="unit_L1500_mla", L=1500, topk=300, qkv_unit=True)
+
+
+# ------------------------------------------------------------------ fold ---
+
+@pytest.mark.parametrize("spec", [gen.TINY_F32, gen.PREFILL_8K, SMALL_MLA], ids=lambda s: s.name)
+def test_fold(dev, spec):
+    say("fold", spec.name)
+    x = gen.make_prefill(spec, seed=1, device=dev)
+    qf, qs = B.dsa_fold_index_query(x["q_idx"], x["q_scale"], x["w"])
+    torch.cuda.synchronize()
+    orc = oracle_prefill(spec, x)
+    if spec.fp8:
+        nbad = P.check_fold_codes(to_np(qf), to_np(qs), orc.qf, orc.qf8, orc.qf_scale)
+        say("fold codes differing at a rounding midpoint:", nbad)
+    else:
+        g = to_np(qf).astype(np.float64)
+        assert np.array_equal(g, orc.qf.astype(np.float32).astype(np.float64))
+
+
+# ---------------------------------------------------------------- scores ---
+
+@pytest.mark.parametrize("spec", [gen.TINY_F32, SMALL_H16, gen.PREFILL_8K, gen.PREFILL_32K], ids=lambda s: s.name)
+def test_index_scores(dev, spec):
+    say("scores", spec.name)
+    x = gen.make_prefill(spec, seed=2, device=dev)
+    qf, qs = B.dsa_fold_index_query(x["q_idx"], x["q_scale"], x["w"])
+    orc = oracle_prefill(spec, x)
+    rows = sample_rows(spec.L, spec.topk, n=16)
+    worst = 0.0
+    for t in rows:
+        g = B.dsa_index_scores(qf, qs, x["k_idx"], x["k_scale"], row_begin=t, row_end=t + 1)
+        worst = max(worst, P.check_scores_row(to_np(g)[0], orc.scores_row(t), t))
+    # a block of rows at once, with a padded leading dimension
+    r0, r1 = max(0, spec.L - 70), spec.L
+    blk = B.dsa_index_scores(qf, qs, x["k_idx"], x["k_scale"], row_begin=r0, row_end=r1, ld=spec.L + 5)
+    blk = to_np(blk)
+    for t in range(r0, r1, 7):
+        P.check_scores_row(blk[t - r0, : spec.L], orc.scores_row(t), t)
+    say("worst normwise row error", worst)
+
+
+def test_index_scores_q_pos(dev):
+    spec = SMALL_H16
+    x = gen.make_prefill(spec, seed=3, device=dev)
+    qf, qs = B.dsa_fold_index_query(x["q_idx"], x["q_scale"], x["w"])
+    pos = torch.tensor(np.random.default_rng(1).integers(0, spec.L, spec.L), dtype=torch.int64, device=dev)
+    g = to_np(B.dsa_index_scores(qf, qs, x["k_idx"], x["k_scale"], q_pos=pos))
+    orc = oracle_prefill(spec, x)
+    pn = pos.cpu().numpy()
+    for t in range(0, spec.L, 37):
+        p = int(pn[t])
+        o = od.index_scores_row(orc.q_vals[t], orc.q_scale_of(t), orc.k_vals, orc.k_scale, p)
+        P.check_scores_row(g[t], o, p)
+
+
+# ------------------------------------------------------------------ top-k ---
+
+@pytest.mark.parametrize("T,S,k,levels", [(64, 100, 1, 64), (64, 5000, 64, 8), (48, 8192, 2048, 64),
+                                           (40, 4000, 4096, 16), (8, 131072, 2048, 64), (30, 3000, 2048, 2)])
+def test_topk_bit_exact(dev, T, S, k, levels):
+    say("topk", T, S, k, levels)
+    pos = torch.tensor(np.random.default_rng(T + S).integers(0, S, T), dtype=torch.int64)
+    pos[0] = S - 1
+    sc = gen.make_scores(T, S, seed=T * 31 + S, q_pos=pos, levels=levels)
+    g = B.dsa_topk(sc.to(dev), k, q_pos=pos.to(dev))
+    cnt = torch.empty(T, dtype=torch.int32, device=dev)
+    g2 = B.dsa_topk(sc.to(dev), k, q_pos=pos.to(dev), count_out=cnt)
+    g, g2, cnt = to_np(g), to_np(g2), to_np(cnt)
+    assert np.array_equal(g, g2)
+    s64 = sc.numpy().astype(np.float64)
+    for t in range(T):
+        n = int(pos[t]) + 1
+        want = od.pad_idx(od.topk_row(s64[t, :n], k), k)
+        assert np.array_equal(g[t], want), (t, n)
+        assert cnt[t] == min(k, n)
+
+
+# -------------------------------------------------------------- attention ---
+
+ATTN_CASES = [
+    ("f32_h4_d64", gen.TINY_F32.with_(L=300), 64),
+    ("bf16_h16_d128", gen.PREFILL_8K.with_(L=3000), 2048),
+    ("bf16_mla", gen.PREFILL_32K.with_(L=2500), 2048),
+    ("bf16_mla_unit", gen.PREFILL_32K.with_(L=2500, qkv_unit=True), 700),
+]
+
+
+@pytest.mark.parametrize("name,spec,k", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_sparse_attn(dev, name, spec, k):
+    say("attn", name)
+    x = gen.make_prefill(spec, seed=4, device=dev)
+    T = 40
+    q = x["q"][:T].contiguous()
+    idx = gen.make_selection(T, spec.L, k, seed=5, min_valid=1)
+    idx[3] = -1                                   # a query with no valid entry
+    idx[5, : min(k, 33)] = torch.arange(min(k, 33), dtype=torch.int32)  # ragged tail of one tile
+    idx[5, min(k, 33):] = -1
+    lse = torch.empty((T, spec.H), dtype=torch.float32, device=dev)
+    out = B.dsa_sparse_attn(q, x["kv"], idx.to(dev), spec.scale, v=x["v"], Dv=spec.Dv, lse_out=lse)
+    g, gl = to_np(out), to_np(lse)
+    if g.dtype == np.uint16:
+        g = od.as_f64(g)
+    kv, vv = to_np(x["kv"]), to_np(x["v"])
+    qn = to_np(q)
+    worst = 0.0
+    for t in range(T):
+        sel = idx[t].numpy()
+        sel = sel[sel >= 0]
+        if sel.size == 0:
+            assert np.all(g[t] == 0) and np.all(np.isneginf(gl[t]))
+            continue
+        kr = od.as_f64(kv[sel])
+        vr = od.as_f64(vv[sel]) if vv is not None else kr[:, : spec.Dv]
+        o, l = od.attend(od.as_f64(qn[t]), kr, vr, spec.scale)
+        worst = max(worst, P.check_attn(g[t], o, f32=spec.attn_f32))
+        assert np.allclose(gl[t], l, rtol=1e-5, atol=1e-5)
+    say("worst", worst)
+
+
+def test_sparse_attn_separate_v_view(dev):
+    """The latent-row reading (V = first Dv entries of the KV row) equals
+    passing that slice as an explicit V with its own leading dimension."""
+    spec = gen.PREFILL_32K.with_(L=600)
+    x = gen.make_prefill(spec, seed=6, device=dev)
+    idx = gen.make_selection(16, spec.L, 256, seed=7, min_valid=1).to(dev)
+    q = x["q"][:16].contiguous()
+    a = B.dsa_sparse_attn(q, x["kv"], idx, spec.scale, v=None, Dv=512)
+    b = B.dsa_sparse_attn(q, x["kv"], idx, spec.scale, v=x["kv"][:, :512], Dv=512)
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------- whole forward ---
+
+def run_forward(spec, x, dev, flags=0):
+    out = torch.empty((spec.L, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
+    idx = torch.empty((spec.L, spec.topk), dtype=torch.int32, device=dev)
+    args = B.forward_args(x, spec.topk, spec.scale, spec.Dv, flags=flags)
+    B.dsa_forward(args, out, idx_out=idx)
+    torch.cuda.synchronize()
+    return out, idx
+
+
+FWD_CASES = [gen.TINY_F32, SMALL_H16, SMALL_MLA, UNIT_MLA, gen.PREFILL_8K, gen.PREFILL_32K]
+
+
+@pytest.mark.parametrize("spec", FWD_CASES, ids=lambda s: s.name)
+def test_forward_prefill(dev, spec):
+    say("forward prefill", spec.name)
+    x = gen.make_prefill(spec, seed=8, device=dev)
+    out, idx = run_forward(spec, x, dev)
+    orc = oracle_prefill(spec, x)
+    rows = list(range(spec.L)) if spec.L <= 1000 else sample_rows(spec.L, spec.topk, n=24)
+    gi = idx.cpu().numpy()
+    diffs = 0
+    worst = 0.0
+    for t in rows:
+        sc = orc.scores_row(t)
+        sel = od.topk_row(sc, spec.topk)
+        d = P.check_topk_row(gi[t], sc, sel, spec.topk)
+        diffs += d
+        if d == 0:
+            o, _ = orc.attend_row(t, sel)
+            g = to_np(out[t])
+            g = od.as_f64(g) if g.dtype == np.uint16 else g.astype(np.float64)
+            worst = max(worst, P.check_attn(g, o, f32=spec.attn_f32))
+    say(f"rows={len(rows)} window-diffs={diffs} worst-attn={worst:.3g}")
+    assert diffs <= max(2, len(rows) // 10)
+
+
+def test_forward_deterministic(dev):
+    spec = SMALL_MLA
+    x = gen.make_prefill(spec, seed=9, device=dev)
+    o1, i1 = run_forward(spec, x, dev)
+    o2, i2 = run_forward(spec, x, dev)
+    assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ----------------------------------------------------------------- decode ---
+
+def run_decode(spec, x, dev):
+    out = torch.empty((spec.B, spec.H, spec.Dv), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((spec.B, spec.topk), dtype=torch.int32, device=dev)
+    args = B.forward_args(x, spec.topk, spec.scale, spec.Dv, mode=B.DSA_MODE_DECODE,
+                          max_len=int(x["lengths"].max()))
+    B.dsa_forward(args, out, idx_out=idx)
+    torch.cuda.synchronize()
+    return out, idx
+
+
+DEC_SMALL = gen.DECODE_64.with_(name="decode_B7_small", B=7, n_min=1, n_max=3000, topk=512)
+
+
+@pytest.mark.parametrize("spec,nseq", [(DEC_SMALL, 7), (gen.DECODE_64, 6)], ids=["small", "B64_full"])
+def test_forward_decode(dev, spec, nseq):
+    say("forward decode", spec.name)
+    lengths = None
+    if spec is DEC_SMALL:
+        lengths = torch.tensor([1, 2, 511, 512, 513, 2999, 1000], dtype=torch.int64)
+    x = gen.make_decode(spec, seed=10, device=dev, lengths=lengths)
+    out, idx = run_decode(spec, x, dev)
+    n = {k: to_np(v) for k, v in x.items() if k not in ("q", "kv")}
+    dec = od.DecodeOracle(n["q_idx"], n["q_scale"], n["k_idx"], n["k_scale"], n["w"], RowsOf(x["q"]),
+                          RowsOf(x["kv"]), None, n["offsets"], spec.topk, spec.scale, spec.Dv)
+    gi = idx.cpu().numpy()
+    rng = np.random.default_rng(0)
+    seqs = sorted(set([0, spec.B - 1] + rng.integers(0, spec.B, nseq).tolist()))
+    diffs = 0
+    for b in seqs:
+        sc = dec.scores_seq(b)
+        sel = od.topk_row(sc, spec.topk)
+        d = P.check_topk_row(gi[b], sc, sel, spec.topk)
+        diffs += d
+        if d == 0:
+            i_o, o, _ = dec.seq(b)
+            P.check_attn(od.as_f64(to_np(out[b])), o)
+    say("decode window diffs", diffs)
+    assert diffs <= 2
