@@ -1,0 +1,238 @@
+"""Throughput of the DSA forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one dsa_forward call over the whole synthetic workload (fold,
+indexer scores, top-k selection and sparse MQA attention), inputs resident in
+HBM.  The headline is the 131072-token causal prefill with k = 2048 and
+MLA-shaped attention (128 heads, key 576, value 512); the 64-sequence batched
+decode step is timed after it.  Prints one JSON line.
+
+The dominant kernel's duration is measured live with HIP events on the stream
+the kernel runs on; its roofline uses algorithmic FLOPs (or bytes) only.  The
+CPU baseline times the fp64 oracle on a bounded random sample of query rows of
+the same workload, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def attn_flops(L, k, H, Dk, Dv):
+    pairs = sum(min(k, t + 1) for t in range(min(L, k))) + max(0, L - k) * k
+    return 2.0 * H * (Dk + Dv) * pairs, pairs
+
+
+def indexer_flops(L):
+    return 2.0 * 128 * L * (L + 1) / 2
+
+
+def kernel_source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparse_attention_long_indexer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, sha):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, valid
+    only while the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    e = d.get(kernel)
+    if not e or e.get("source_sha") != sha:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(spec, x, rows=48, seed=0):
+    """Time the fp64 oracle on `rows` query rows drawn uniformly from the
+    workload; the per-row mean estimates the whole prefill's CPU time."""
+    import numpy as np
+    import torch
+
+    import oracle.dsa as od
+
+    def np_(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    class Rows:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, i):
+            return np_(self.t[i])
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rng = np.random.default_rng(seed)
+    sample = rng.integers(0, spec.L, rows)
+    t0 = time.perf_counter()
+    orc = od.PrefillOracle(np_(x["q_idx"]), np_(x["q_scale"]), np_(x["k_idx"]), np_(x["k_scale"]), np_(x["w"]),
+                           Rows(x["q"]), np_(x["kv"]), None if x["v"] is None else np_(x["v"]), spec.topk,
+                           spec.scale, spec.Dv)
+    t_setup = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    for t in sample:
+        orc.row(int(t))
+    t_rows = time.perf_counter() - t1
+    per_row = t_rows / rows
+    total = t_setup + per_row * spec.L
+    return {"value": spec.L / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} query rows drawn uniformly from the {spec.L}-token prefill "
+                      f"(setup {t_setup:.1f} s + {t_rows:.1f} s for the rows, extrapolated by the row mean)",
+            "seconds": round(t_setup + t_rows, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill_L131072_mla")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the prefill shards by query rows, decode by sequence; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_long_indexer_amd import binding as B
+    from sparse_attention_long_indexer_amd import inputs as gen
+
+    B.lib()
+    dev = torch.device("cuda:0")
+    spec = gen.WORKLOADS[args.workload]
+    log("workload", spec.name, "generating inputs")
+    x = gen.make_prefill(spec, seed=0, device=dev)
+    L, k = spec.L, spec.topk
+    out = torch.empty((L, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
+    idx = torch.empty((L, k), dtype=torch.int32, device=dev)
+    fa = B.forward_args(x, k, spec.scale, spec.Dv)
+    ws = torch.empty(max(B.dsa_forward_workspace_size(fa), 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        B.dsa_forward(fa, out, idx_out=idx, ws=ws)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    tok_s = L / dt
+    log(f"prefill {dt * 1e3:.2f} ms/step, {tok_s:.4g} tokens/s")
+
+    # dominant kernel (sparse attention) timed alone with HIP events on the
+    # stream it is launched on (torch's current stream, passed to the library)
+    st = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(2, args.steps)
+    B.dsa_sparse_attn(x["q"], x["kv"], idx, spec.scale, v=x["v"], Dv=spec.Dv, out=out)
+    ev0.record(st)
+    for _ in range(reps):
+        B.dsa_sparse_attn(x["q"], x["kv"], idx, spec.scale, v=x["v"], Dv=spec.Dv, out=out)
+    ev1.record(st)
+    torch.cuda.synchronize()
+    attn_ms = ev0.elapsed_time(ev1) / reps
+    flops, pairs = attn_flops(L, k, spec.H, spec.Dk, spec.Dv)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    sha = kernel_source_sha(["attn.hip", "common.h"])
+    traffic = load_traffic("attn_bf16_kernel<576,512,8>", sha)
+    roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<576,512,8>", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic, "ms_per_launch": round(attn_ms, 3),
+            "algorithmic_flops_per_launch": flops, "selected_pairs": pairs}
+    idx_ms = dt * 1e3 - attn_ms
+    ifl = indexer_flops(L)
+    roof_idx = {"bound": "mfma", "stage": "fold + indexer scores + top-k (forward minus attention)",
+                "ms": round(idx_ms, 3), "achieved": round(ifl / (idx_ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ifl / (idx_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+    log(f"attention {attn_ms:.2f} ms/launch = {achieved:.1f} TFLOP/s; indexer+select {idx_ms:.2f} ms")
+
+    result = {
+        "metric": "DSA prefill tokens/s at L=128K, k=2048",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "dtype_detail": "indexer e4m3 x e4m3 -> fp32 MFMA; attention bf16 -> fp32 MFMA",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "L": L, "topk": k, "heads": spec.H, "dk": spec.Dk, "dv": spec.Dv,
+                   "batch": 1, "index_dim": 128},
+        "roofline": roof, "roofline_indexer": roof_idx,
+    }
+    del out, idx, ws
+
+    if not args.no_decode:
+        ds = gen.DECODE_64
+        log("decode: generating inputs")
+        xd = gen.make_decode(ds, seed=0, device=dev)
+        dout = torch.empty((ds.B, ds.H, ds.Dv), dtype=torch.bfloat16, device=dev)
+        didx = torch.empty((ds.B, ds.topk), dtype=torch.int32, device=dev)
+        da = B.forward_args(xd, ds.topk, ds.scale, ds.Dv, mode=B.DSA_MODE_DECODE,
+                            max_len=int(xd["lengths"].max()))
+        dws = torch.empty(max(B.dsa_forward_workspace_size(da), 256), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            B.dsa_forward(da, dout, idx_out=didx, ws=dws)
+        torch.cuda.synchronize()
+        reps = 20
+        ev0.record(st)
+        for _ in range(reps):
+            B.dsa_forward(da, dout, idx_out=didx, ws=dws)
+        ev1.record(st)
+        torch.cuda.synchronize()
+        dms = ev0.elapsed_time(ev1) / reps
+        n = xd["lengths"]
+        byts = float(n.sum()) * 132 + float(torch.clamp(n, max=ds.topk).sum()) * ds.Dk * 2 \
+            + ds.B * ds.H * (ds.Dk + ds.Dv) * 2 + 2 * ds.B * ds.topk * 4
+        result["decode"] = {"workload": ds.name, "queries_per_s": round(ds.B / (dms * 1e-3), 1),
+                            "ms_per_step": round(dms, 4), "algorithmic_bytes": byts,
+                            "roofline": {"bound": "hbm", "achieved": round(byts / (dms * 1e-3) / 1e9, 1),
+                                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                         "frac": round(byts / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                         "note": "warm caches; whole decode step"}}
+        log(f"decode {dms:.3f} ms/step")
+        del xd, dout, didx, dws
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(spec, x, rows=args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
