@@ -64,9 +64,13 @@ typedef enum {
   DSA_MODE_DECODE = 1
 } dsa_mode_t;
 
-/* dsa_forward flags */
-#define DSA_FLAG_MATERIALIZE 1u /* use the materialised score + select path
-                                   even where the fused one would run */
+/* dsa_forward flags (the result is the same on every path) */
+#define DSA_FLAG_MATERIALIZE 1u   /* materialise the scores and run dsa_topk's
+                                     select even where the fused path runs */
+#define DSA_FLAG_FUSED 2u         /* fused scores + select even for short
+                                     prefills (FP8 index only) */
+#define DSA_FLAG_FORCE_FALLBACK 4u /* fused path: settle every long row with
+                                     the exact recompute fallback (testing) */
 
 int dsa_abi_version(void);
 const char* dsa_status_str(dsa_status_t s);

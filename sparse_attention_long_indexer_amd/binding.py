@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libdsa.so")
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_MODE_PREFILL, DSA_MODE_DECODE = 0, 1
 DSA_FLAG_MATERIALIZE = 1
+DSA_FLAG_FUSED = 2
+DSA_FLAG_FORCE_FALLBACK = 4
 INDEX_DIM = 128
 MAX_TOPK = 4096
 

@@ -93,7 +93,16 @@ dsa_status_t check_attn(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dty
 struct FwdPlan {
   size_t qf_off, qs_off, idx_off, sc_off, total;
   int64_t chunk_rows;  // prefill: rows of scores materialised at once
+  bool fused;          // prefill: fused scores + select
 };
+
+constexpr int64_t kFusedMinT = 4096;  // shorter prefills materialise their scores
+
+bool use_fused(const dsa_forward_args* a) {
+  return a->mode == DSA_MODE_PREFILL && a->idx_dtype == DSA_FP8_E4M3 &&
+         !(a->flags & DSA_FLAG_MATERIALIZE) && index_select_supported(a->T, a->T) &&
+         (a->T >= kFusedMinT || (a->flags & DSA_FLAG_FUSED));
+}
 
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreChunkBytes = size_t(1) << 31;  // cap on one score slab
@@ -110,7 +119,11 @@ FwdPlan plan_forward(const dsa_forward_args* a, bool need_idx) {
   p.idx_off = off;
   if (need_idx) off = round_up(off + (size_t)R * (size_t)a->topk * 4, kAlign);
   p.sc_off = off;
-  if (a->mode == DSA_MODE_PREFILL) {
+  p.fused = use_fused(a);
+  if (p.fused) {
+    p.chunk_rows = R;
+    off = round_up(off + index_select_workspace_bytes(a->T, a->T), kAlign);
+  } else if (a->mode == DSA_MODE_PREFILL) {
     const int64_t S = a->T;
     int64_t rows = S > 0 ? (int64_t)(kScoreChunkBytes / ((size_t)S * 4)) : 1;
     rows = rows / 64 * 64;
@@ -307,7 +320,13 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
     at.out = out;
     at.lse = nullptr;
 
-    if (a->mode == DSA_MODE_PREFILL) {
+    if (p.fused) {
+      e = launch_index_select((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale, R, R, a->topk, idx,
+                              sc, (a->flags & DSA_FLAG_FORCE_FALLBACK) != 0, st);
+      if (e != hipSuccess) return DSA_ERR_DEVICE;
+      at.seq_offsets = nullptr;
+      at.S = R;
+    } else if (a->mode == DSA_MODE_PREFILL) {
       const int64_t S = R;
       for (int64_t r0 = 0; r0 < R; r0 += p.chunk_rows) {
         const int64_t r1 = r0 + p.chunk_rows < R ? r0 + p.chunk_rows : R;

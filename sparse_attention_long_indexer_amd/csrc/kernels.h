@@ -36,6 +36,13 @@ size_t topk_workspace_bytes(int64_t rows, int64_t max_n, int64_t k);
 hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k, int32_t* idx_out,
                        int32_t* count_out, void* ws, hipStream_t st);
 
+// index_select.hip: fused scores + top-k for causal prefill (queries = keys)
+bool index_select_supported(int64_t T, int64_t S);
+size_t index_select_workspace_bytes(int64_t T, int64_t S);
+hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t* k8, const float* ks,
+                               int64_t T, int64_t S, int64_t topk, int32_t* idx_out, void* ws,
+                               bool force_fallback, hipStream_t st);
+
 // attn.hip
 struct AttnArgs {
   const void* q;        // [T][H][Dk]

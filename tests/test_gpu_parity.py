@@ -272,3 +272,45 @@ def test_forward_decode(dev, spec, nseq):
             P.check_attn(od.as_f64(to_np(out[b])), o)
     say("decode window diffs", diffs)
     assert diffs <= 2
+
+
+# ------------------------------------------------- fused indexer + select ---
+
+def forward_idx(spec, x, dev, flags):
+    idx = torch.empty((spec.L, spec.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((spec.L, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
+    B.dsa_forward(B.forward_args(x, spec.topk, spec.scale, spec.Dv, flags=flags), out, idx_out=idx)
+    torch.cuda.synchronize()
+    return idx, out
+
+
+FUSED_CASES = [gen.PREFILL_8K.with_(L=5000, topk=700), gen.PREFILL_8K.with_(L=6001, topk=2048),
+               gen.PREFILL_8K, gen.PREFILL_32K, gen.PREFILL_128K]
+
+
+@pytest.mark.parametrize("spec", FUSED_CASES, ids=lambda s: f"L{s.L}_k{s.topk}")
+def test_fused_select_equals_materialized(dev, spec):
+    """The fused scores + select path returns exactly what materialised
+    scores + the standalone radix select return (same fp32 scores)."""
+    say("fused vs materialized", spec.L, spec.topk)
+    x = gen.make_prefill(spec, seed=11, device=dev)
+    i_f, o_f = forward_idx(spec, x, dev, B.DSA_FLAG_FUSED)
+    i_m, o_m = forward_idx(spec, x, dev, B.DSA_FLAG_MATERIALIZE)
+    bad = (i_f != i_m).any(dim=1).nonzero().flatten()
+    assert bad.numel() == 0, bad[:10].tolist()
+    assert torch.equal(o_f.view(torch.int16), o_m.view(torch.int16))
+    if spec.L >= 131072:
+        # full-size sampled rows against the oracle as well
+        orc = oracle_prefill(spec, x)
+        gi = i_f.cpu().numpy()
+        for t in sample_rows(spec.L, spec.topk, n=6, seed=3):
+            sc = orc.scores_row(t)
+            P.check_topk_row(gi[t], sc, od.topk_row(sc, spec.topk), spec.topk)
+
+
+def test_fused_forced_fallback(dev):
+    spec = gen.PREFILL_8K.with_(L=6000, topk=1024)
+    x = gen.make_prefill(spec, seed=12, device=dev)
+    i_f, _ = forward_idx(spec, x, dev, B.DSA_FLAG_FUSED | B.DSA_FLAG_FORCE_FALLBACK)
+    i_m, _ = forward_idx(spec, x, dev, B.DSA_FLAG_MATERIALIZE)
+    assert torch.equal(i_f, i_m)
