@@ -60,14 +60,15 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
 }
 
 // ---- 1. threshold estimate ------------------------------------------------
-__global__ __launch_bounds__(256) void idx_estimate_kernel(const uint8_t* __restrict__ qf,
+constexpr int kEstWaves = 16;
+__global__ __launch_bounds__(kEstWaves * 64) void idx_estimate_kernel(const uint8_t* __restrict__ qf,
                                                            const float* __restrict__ qs,
                                                            const uint8_t* __restrict__ k8,
                                                            const float* __restrict__ ks, int64_t T,
                                                            int64_t S, int64_t topk,
                                                            float* __restrict__ tau) {
   __shared__ uint16_t sc[16][kSampleMax];
-  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t hist[kEstWaves][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int64_t R0 = (int64_t)blockIdx.x * 16;
@@ -79,25 +80,37 @@ __global__ __launch_bounds__(256) void idx_estimate_kernel(const uint8_t* __rest
   float qsc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) qsc[i] = qs[min(R0 + 4 * g + i, T - 1)];
-  for (int64_t j16 = w; j16 * 16 < nsb; j16 += 4) {
-    const int64_t j = j16 * 16 + c;
-    int64_t s = j * P + sample_off(j, P);
-    s = s < S ? s : S - 1;
-    const v8i b = *(const v8i*)(k8 + s * kIdxDim + 32 * g);
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma_fp8_16x16x128(a, b, acc);
-    const float kss = ks[s];
+  // each wave takes sample tiles w, w+16, ...; four tiles' keys are loaded
+  // before their MFMAs so the loads overlap
+  for (int64_t j0 = (int64_t)w * 16; j0 < nsb; j0 += 4 * kEstWaves * 16) {
+    v8i b[4];
+    float kss[4];
+    int64_t jj[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float u = acc[i] * kss * qsc[i];
-      sc[4 * g + i][j] = (uint16_t)(__float_as_uint(u > 0.f ? u : 0.f) >> 16);
+    for (int u = 0; u < 4; ++u) {
+      jj[u] = j0 + (int64_t)u * kEstWaves * 16 + c;
+      int64_t sk = jj[u] * P + sample_off(jj[u], P);
+      sk = sk < S ? sk : S - 1;
+      b[u] = *(const v8i*)(k8 + sk * kIdxDim + 32 * g);
+      kss[u] = ks[sk];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (j0 + (int64_t)u * kEstWaves * 16 >= nsb) break;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_fp8_16x16x128(a, b[u], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float uu = acc[i] * kss[u] * qsc[i];
+        sc[4 * g + i][jj[u]] = (uint16_t)(__float_as_uint(uu > 0.f ? uu : 0.f) >> 16);
+      }
     }
   }
   __syncthreads();
 
   uint32_t* h = hist[w];
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = 4 * w + rr;
+  for (int rr = 0; rr < 16 / kEstWaves; ++rr) {
+    const int row = (16 / kEstWaves) * w + rr;
     const int64_t t = R0 + row;
     if (t >= T) break;
     const int64_t n = min(t + 1, S);
@@ -122,10 +135,16 @@ __global__ __launch_bounds__(256) void idx_estimate_kernel(const uint8_t* __rest
           key = sc[row][i];
           in = pass == 0 || (key >> 8) == (prefix >> 8);
         }
-        const bool z = in && key == 0;
-        const uint64_t zb = ballot(z);
-        if (in && !z) atomicAdd(&h[(key >> shift) & 255u], 1u);
-        if (zb && lane == 0) atomicAdd(&h[0], (uint32_t)__popcll(zb));
+        // peel the wave's most common digit (zeros and clustered scores)
+        const uint32_t dg = (key >> shift) & 255u;
+        const uint64_t act = ballot(in);
+        if (act) {
+          const int first = __builtin_ctzll(act);
+          const uint32_t d0 = __shfl(dg, first);
+          const uint64_t same = ballot(in && dg == d0);
+          if (lane == first) atomicAdd(&h[d0], (uint32_t)__popcll(same));
+          if (in && dg != d0) atomicAdd(&h[dg], 1u);
+        }
       }
       __builtin_amdgcn_wave_barrier();
       // digit of the remaining-th largest
@@ -159,14 +178,64 @@ __global__ __launch_bounds__(256) void idx_estimate_kernel(const uint8_t* __rest
       prefix |= dig << shift;
       __builtin_amdgcn_wave_barrier();
     }
+    // a zero rank-r sample means the row has few positive scores: keep the
+    // positive ones (tau = the smallest positive float)
     const float tv = __uint_as_float(prefix << 16);
-    if (lane == 0) tau[t] = tv > 0.f ? tv : -INFINITY;
+    if (lane == 0) tau[t] = tv > 0.f ? tv : 1.17549435e-38f;
   }
 }
 
 // ---- 2. filter pass ---------------------------------------------------------
 constexpr int kFiltKeys = 64;             // keys per LDS tile
 constexpr int kFiltRows = 256;            // queries per block (64 per wave)
+constexpr int kSets = 2;                  // key chunks per row (long rows split in two)
+constexpr int kSlack = 16;                // sink slots past kCap (one tile's worth per lane)
+constexpr int kSegStride = kCap + kSlack;
+
+// Work items: long row blocks (keys past the chunk boundary kmax) are split
+// into chunk 0 = keys [0, kmax) and chunk 1 = keys [kmax, end), each with its
+// own survivor set, so no item scans more than kmax keys.  Items are ordered
+// longest first.
+struct FilterItem {
+  int64_t rb;    // row block
+  int set;       // key chunk / survivor set
+  int64_t k0, k1;
+};
+__device__ __forceinline__ FilterItem filter_item(int64_t id, int64_t T, int64_t S, int64_t kmax) {
+  const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
+  // row blocks whose key range passes kmax
+  const int64_t first_long = kmax / kFiltRows;  // block rb sees keys < min(T, (rb+1)*256)
+  const int64_t nl = nb > first_long ? nb - first_long : 0;
+  FilterItem it;
+  if (id < nl) {
+    it.rb = nb - 1 - id;
+    it.set = 0;
+  } else if (id < 2 * nl) {
+    it.rb = nb - 1 - (id - nl);
+    it.set = 1;
+  } else {
+    it.rb = nb - 1 - (id - nl);
+    it.set = 0;
+  }
+  const int64_t end = min(S, min(T, (it.rb + 1) * kFiltRows));
+  if (it.rb >= first_long) {
+    it.k0 = it.set ? kmax : 0;
+    it.k1 = it.set ? end : min(end, kmax);
+  } else {
+    it.k0 = 0;
+    it.k1 = end;
+  }
+  return it;
+}
+__host__ __device__ inline int64_t filter_kmax(int64_t T) {
+  const int64_t h = (T + 1) / 2;
+  return (h + kFiltRows - 1) / kFiltRows * kFiltRows;
+}
+inline int64_t filter_items(int64_t T) {
+  const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
+  const int64_t first_long = filter_kmax(T) / kFiltRows;
+  return nb + (nb > first_long ? nb - first_long : 0);
+}
 
 __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
@@ -176,15 +245,15 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
   __shared__ __align__(16) float kst[2][kFiltKeys];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  // longest rows first for a better tail
-  const int64_t nblk = (T + kFiltRows - 1) / kFiltRows;
-  const int64_t R0 = (nblk - 1 - (int64_t)blockIdx.x) * kFiltRows;
+  const FilterItem item = filter_item(blockIdx.x, T, S, filter_kmax(T));
+  const int64_t R0 = item.rb * kFiltRows;
   const int64_t Q0 = R0 + 64 * w;
 
   v8i bq[4];
-  int64_t tq[4];
+  int tq[4];
   float tv[4];
-  int cnt[4];
+  uint32_t cnt[4];
+  bool ovf[4];
   uint2* seg[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -192,20 +261,20 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
     const bool ok = t < T;
     const int64_t tt = ok ? t : T - 1;
     bq[q] = *(const v8i*)(qf + tt * kIdxDim + 32 * g);
-    tq[q] = ok ? t : -1;  // an invalid query masks every key
+    tq[q] = ok ? (int)t : -1;  // an invalid query masks every key
     const float ta = tau[tt];
     // survivors need v * qs >= tau; shave a few ulps so rounding of the
     // product can never drop a key whose final score reaches tau
     tv[q] = !ok ? INFINITY : ta == -INFINITY ? -INFINITY : (ta / qs[tt]) * (1.0f - 1.0f / (1 << 20));
     cnt[q] = 0;
-    seg[q] = cand + ((tt * kSeg) + g) * (int64_t)kCap;
+    ovf[q] = false;
+    seg[q] = cand + ((tt * kSets + item.set) * kSeg + g) * (int64_t)kSegStride;
   }
-  const int64_t kend = min(S, min(R0 + kFiltRows, T));  // keys any row of the block can see
-  const int ntiles = (int)((kend + kFiltKeys - 1) / kFiltKeys);
+  const int ntiles = (int)((item.k1 - item.k0 + kFiltKeys - 1) / kFiltKeys);
 
   // tile loader: 64 keys x 128 B = 512 chunks (2 per thread) + 64 scales
   auto issue = [&](int it, int buf) {
-    const int64_t kb = (int64_t)it * kFiltKeys;
+    const int64_t kb = item.k0 + (int64_t)it * kFiltKeys;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int chunk = (i * 4 + w) * 64 + lane;       // 16-byte chunk of the tile
@@ -230,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
 
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
-    const int64_t kb = (int64_t)it * kFiltKeys;
+    const int64_t kb = item.k0 + (int64_t)it * kFiltKeys;
     if (it + 1 < ntiles) issue(it + 1, buf ^ 1);
     if (kb + kFiltKeys > S) {  // partial last tile: fill its scales by hand
       for (int i = threadIdx.x; i < kFiltKeys; i += 256) {
@@ -239,15 +308,26 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
       }
       __syncthreads();
     }
+    // a segment grows by at most 16 per tile: clamp once per tile into the
+    // sink slots past kCap and remember the overflow
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (cnt[q] > (uint32_t)kCap) {
+        ovf[q] = true;
+        cnt[q] = kCap;
+      }
+    }
     const bool mask = kb + kFiltKeys - 1 > Q0;  // some key may lie past a query of this wave
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const int64_t k16 = kb + 16 * kt;
+      const int k16 = (int)(kb + 16 * kt);
       const int rot = tile_rot(k16 >> 4);
       const int ar = (c + rot) & 15;                  // A row c holds key k16 + ar
-      const uint8_t* ap = ktile[buf] + (16 * kt + ar) * kIdxDim + 32 * g;
-      const v8i a = *(const v8i*)ap;
-      int64_t key[4];
+      const v8i a = *(const v8i*)(ktile[buf] + (16 * kt + ar) * kIdxDim + 32 * g);
+      v4f acc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = mfma_fp8_16x16x128(a, bq[q], (v4f){0.f, 0.f, 0.f, 0.f});
+      int key[4];
       float kss[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -255,48 +335,63 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
         key[i] = k16 + kr;
         kss[i] = kst[buf][16 * kt + kr];
       }
+      if (mask) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma_fp8_16x16x128(a, bq[q], acc);
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = acc[i] * kss[i];
-          bool pass = v >= tv[q];
-          if (mask) pass = pass && key[i] <= tq[q];
-          if (pass) {
-            if (cnt[q] < kCap) seg[q][cnt[q]] = make_uint2(__float_as_uint(v), (uint32_t)key[i]);
-            ++cnt[q];
+          for (int i = 0; i < 4; ++i) {
+            const float v = acc[q][i] * kss[i];
+            const bool pass = (v >= tv[q]) & (key[i] <= tq[q]);
+            if (pass) seg[q][cnt[q]] = make_uint2(__float_as_uint(v), (uint32_t)key[i]);
+            cnt[q] += pass ? 1u : 0u;
           }
-        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = acc[q][i] * kss[i];
+            const bool pass = v >= tv[q];
+            if (pass) seg[q][cnt[q]] = make_uint2(__float_as_uint(v), (uint32_t)key[i]);
+            cnt[q] += pass ? 1u : 0u;
+          }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  const bool two = item.rb >= filter_kmax(T) / kFiltRows;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (tq[q] >= 0) cnt_out[tq[q] * kSeg + g] = cnt[q];
+  for (int q = 0; q < 4; ++q) {
+    if (tq[q] < 0) continue;
+    const int v = (ovf[q] || cnt[q] > (uint32_t)kCap) ? kCap + 1 : (int)cnt[q];
+    cnt_out[((int64_t)tq[q] * kSets + item.set) * kSeg + g] = v;
+    if (!two) cnt_out[((int64_t)tq[q] * kSets + 1) * kSeg + g] = 0;  // rows with one key chunk
+  }
 }
 
 // ---- 3. exact select over survivors ---------------------------------------
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelMax = 6144;             // survivor slots a row may stage in LDS
+constexpr int kChunk = 64;                // survivors per 512-byte direct-to-LDS copy
+constexpr int kMaxChunks = kSelMax / kChunk;
+constexpr int kMaxTies = 512;             // keys equal to the m-th best kept in a list
 
 __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
     const float* __restrict__ qs, const float* __restrict__ tau, const uint2* __restrict__ cand,
     const int32_t* __restrict__ cnt_in, int64_t T, int64_t S, int64_t topk, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ fb, int force_fallback) {
   extern __shared__ __align__(16) uint32_t sm[];
-  uint32_t* ckey = sm;                          // [kSeg*kCap] score keys
-  int32_t* cidx = (int32_t*)(sm + kSeg * kCap); // [kSeg*kCap] key positions
-  uint32_t* bm = sm + 2 * kSeg * kCap;          // [2][nwords] bitmaps: selected, tied
-  __shared__ uint32_t hist[256];
+  uint2* cl = (uint2*)sm;                       // [kSelMax] (score key, position) pairs
+  uint32_t* sel = sm + 2 * kSelMax;             // [nwords] bitmap of kept positions
+  __shared__ uint32_t hist[1024];
   __shared__ uint32_t wave_cnt[kSelWaves];
   __shared__ uint32_t s_sel[2];
-  __shared__ int s_off[kSeg + 1];
-  __shared__ int s_bad;
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ int s_cnt[kSets * kSeg], s_cbase[kSets * kSeg + 1];
+  __shared__ int32_t s_tie[kMaxTies];
+  __shared__ int s_ntie, s_bad;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t = blockIdx.x;
   const int64_t n = min(t + 1, S);
   const int64_t m = min(topk, n);
@@ -305,150 +400,132 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
     for (int64_t i = tid; i < topk; i += kSelThreads) o[i] = i < n ? (int32_t)i : -1;
     return;
   }
+  const float qsc = qs[t];
+  const float tt = tau[t];
   const int nwords = (int)((n + 31) >> 5);
+  if (tid < kSets * kSeg) s_cnt[tid] = cnt_in[t * kSets * kSeg + tid];
+  if (tid == 0) s_ntie = 0;
+  for (int i = tid; i < nwords; i += kSelThreads) sel[i] = 0;
+  __syncthreads();
+  // chunk layout: segment gq owns chunks [s_cbase[gq], s_cbase[gq+1])
   if (tid == 0) {
-    int off = 0, bad = 0;
-    for (int gq = 0; gq < kSeg; ++gq) {
-      const int cq = cnt_in[t * kSeg + gq];
+    int nch = 0, bad = 0, total = 0;
+    for (int gq = 0; gq < kSets * kSeg; ++gq) {
+      const int cq = s_cnt[gq];
       if (cq > kCap) bad = 1;
-      s_off[gq] = off;
-      off += cq > kCap ? kCap : cq;
+      const int cv = cq > kCap ? kCap : cq;
+      total += cv;
+      s_cbase[gq] = nch;
+      nch += (cv + kChunk - 1) / kChunk;
     }
-    s_off[kSeg] = off;
-    s_bad = bad;
+    s_cbase[kSets * kSeg] = nch;
+    s_bad = bad || nch > kMaxChunks || (tt == -INFINITY && total != n);
   }
   __syncthreads();
-  const int total = s_off[kSeg];
-  const float tt = tau[t];
-  if (s_bad || force_fallback || (tt == -INFINITY && total != n)) {
+  if (s_bad || force_fallback) {
     if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
     return;
   }
-  // load survivors, final score u = v * qs with ReLU
-  const float qsc = qs[t];
-  uint32_t nge = 0;
-  for (int e = tid; e < total; e += kSelThreads) {
+  const int nch = s_cbase[kSets * kSeg];
+  // stage: one 512-byte direct-to-LDS copy (32 lanes x 16 B) per chunk;
+  // reads past a segment's count stay inside its kSegStride slots
+  for (int ch = 2 * w + (lane >> 5); ch < nch; ch += 2 * kSelWaves) {
     int gq = 0;
-    while (gq + 1 < kSeg && e >= s_off[gq + 1]) ++gq;
-    const uint2 cv = cand[(t * kSeg + gq) * (int64_t)kCap + (e - s_off[gq])];
-    const float u0 = __uint_as_float(cv.x) * qsc;
-    const float u = u0 > 0.f ? u0 : 0.f;
-    ckey[e] = score_key(u);
-    cidx[e] = (int32_t)cv.y;
-    nge += (u >= tt) ? 1u : 0u;
+    while (gq + 1 < kSets * kSeg && ch >= s_cbase[gq + 1]) ++gq;
+    const int ofs = (ch - s_cbase[gq]) * kChunk;
+    const uint2* src = cand + (t * kSets * kSeg + gq) * (int64_t)kSegStride + ofs + 2 * (lane & 31);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)src,
+        (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint2*)cl +
+                                                  (ch & ~1) * kChunk),
+        16, 0, 0);
   }
-  for (int i = tid; i < 2 * nwords; i += kSelThreads) bm[i] = 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // final score u = v * qs with ReLU; invalid slots get key 0 (below every
+  // real score key, all of which are >= key(+0.0))
+  const int nslots = nch * kChunk;
+  uint32_t nge = 0, mx = 0u, mn = 0xFFFFFFFFu;
+  for (int e = tid; e < nslots; e += kSelThreads) {
+    const int ch = e / kChunk;
+    int gq = 0;
+    while (gq + 1 < kSets * kSeg && ch >= s_cbase[gq + 1]) ++gq;
+    const int valid = min(kChunk, min(s_cnt[gq], kCap) - (ch - s_cbase[gq]) * kChunk);
+    const uint2 cv = cl[e];
+    uint32_t key = 0;
+    if ((e & (kChunk - 1)) < valid) {
+      const float u0 = __uint_as_float(cv.x) * qsc;
+      const float u = u0 > 0.f ? u0 : 0.f;
+      key = score_key(u);
+      nge += (u >= tt) ? 1u : 0u;
+      mx = max(mx, key);
+      mn = min(mn, key);
+    }
+    cl[e].x = key;
+  }
   {
-    uint32_t tot;
-    // every survivor already holds v >= tau/qs (rounded down), but only the
-    // ones whose final score reaches tau count towards the proof
     nge = wave_sum(nge);
-    if (lane == 0) wave_cnt[tid >> 6] = nge;
+    mx = wave_max(mx);
+    mn = wave_min(mn);
+    if (lane == 0) {
+      wave_cnt[w] = nge;
+      hist[w] = mx;
+      hist[16 + w] = mn;
+    }
     __syncthreads();
-    tot = 0;
-    for (int i = 0; i < kSelWaves; ++i) tot += wave_cnt[i];
+    uint32_t tot = 0;
+    mx = 0u;
+    mn = 0xFFFFFFFFu;
+    for (int i = 0; i < kSelWaves; ++i) {
+      tot += wave_cnt[i];
+      mx = max(mx, hist[i]);
+      mn = min(mn, hist[16 + i]);
+    }
     __syncthreads();
+    // survivors reaching tau prove the answer is among them
     if (tt != -INFINITY && tot < (uint32_t)m) {
       if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
       return;
     }
   }
-  // radix select of the m-th best key among the survivors
-  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)m;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    const uint32_t zdig = (kZeroKey >> shift) & 255u;
-    for (int e0 = 0; e0 < total; e0 += kSelThreads) {
-      const int e = e0 + tid;
-      bool in = false;
-      uint32_t key = 0;
-      if (e < total) {
-        key = ckey[e];
-        in = (key & mask) == prefix;
-      }
-      const bool z = in && key == kZeroKey;
-      const uint64_t zb = ballot(z);
-      if (in && !z) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      if (zb && lane == 0) atomicAdd(&hist[zdig], (uint32_t)__popcll(zb));
+  // the m-th best key lies in [key(tau), max] (or [min, max] when every key
+  // was kept)
+  const uint32_t lo = tt != -INFINITY ? score_key(tt) : mn;
+  uint32_t thr, need;
+  radix_select<kSelThreads>([&](int64_t e) { return cl[e].x; }, nslots, (uint32_t)m, lo, mx, hist, wave_cnt,
+                            s_sel, thr, need);
+  // keys above the m-th best go to the bitmap; ties go to a list
+  for (int e = tid; e < nslots; e += kSelThreads) {
+    const uint2 cv = cl[e];
+    const uint32_t key = cv.x;
+    const int32_t p = (int32_t)cv.y;
+    if (key < thr || p < 0 || p >= n) continue;  // also skips invalid slots (key 0)
+    if (key > thr) {
+      atomicOr(&sel[p >> 5], 1u << (p & 31));
+    } else {
+      const int q = atomicAdd(&s_ntie, 1);
+      if (q < kMaxTies) s_tie[q] = p;
     }
-    __syncthreads();
-    if (tid < 64) {
-      uint32_t c4[4], sum = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c4[e] = hist[255 - 4 * tid - e];
-        sum += c4[e];
-      }
-      uint32_t incl = sum;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off);
-        if (tid >= off) incl += v;
-      }
-      uint32_t above = incl - sum;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (above < remaining && remaining <= above + c4[e]) {
-          s_sel[0] = 255u - 4u * tid - e;
-          s_sel[1] = above;
-        }
-        above += c4[e];
-      }
-    }
-    __syncthreads();
-    remaining -= s_sel[1];
-    prefix |= s_sel[0] << shift;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  const uint32_t thr = prefix, need = remaining;
-  uint32_t* sel = bm;
-  uint32_t* tie = bm + nwords;
-  for (int e = tid; e < total; e += kSelThreads) {
-    const uint32_t key = ckey[e];
-    const int32_t p = cidx[e];
-    if (p < 0 || p >= n) continue;
-    if (key > thr) atomicOr(&sel[p >> 5], 1u << (p & 31));
-    else if (key == thr) atomicOr(&tie[p >> 5], 1u << (p & 31));
   }
   __syncthreads();
-  // keep the `need` lowest-position ties: prefix popcount over tie words
+  const int ntie = s_ntie;
+  if (ntie > kMaxTies) {  // a pathological tie at the boundary: settle exactly elsewhere
+    if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
+    return;
+  }
+  // keep the `need` lowest-position ties
+  for (int i = tid; i < ntie; i += kSelThreads) {
+    const int32_t p = s_tie[i];
+    int rank = 0;
+    for (int j = 0; j < ntie; ++j) rank += s_tie[j] < p ? 1 : 0;
+    if (rank < (int)need) atomicOr(&sel[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // ascending output: prefix popcount over the bitmap
   const int per = (nwords + kSelThreads - 1) / kSelThreads;
   const int w0 = tid * per, w1 = min(nwords, w0 + per);
   uint32_t mine = 0;
-  for (int i = w0; i < w1; ++i) mine += __popc(tie[i]);
-  uint32_t tot_tie;
-  {
-    // exclusive block prefix of `mine`
-    uint32_t incl = mine;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) wave_cnt[tid >> 6] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    tot_tie = 0;
-    for (int i = 0; i < kSelWaves; ++i) {
-      before += (i < (tid >> 6)) ? wave_cnt[i] : 0u;
-      tot_tie += wave_cnt[i];
-    }
-    __syncthreads();
-    uint32_t run = before + incl - mine;
-    for (int i = w0; i < w1; ++i) {
-      uint32_t wv = tie[i];
-      while (wv) {
-        const uint32_t b = wv & (0u - wv);
-        if (run < need) sel[i] |= b;
-        ++run;
-        wv ^= b;
-      }
-    }
-  }
-  __syncthreads();
-  // ascending output: prefix popcount over the selected bitmap
-  mine = 0;
   for (int i = w0; i < w1; ++i) mine += __popc(sel[i]);
   {
     uint32_t incl = mine;
@@ -456,10 +533,10 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
       const uint32_t v = __shfl_up(incl, off);
       if (lane >= off) incl += v;
     }
-    if (lane == 63) wave_cnt[tid >> 6] = incl;
+    if (lane == 63) wave_cnt[w] = incl;
     __syncthreads();
     uint32_t before = 0;
-    for (int i = 0; i < kSelWaves; ++i) before += (i < (tid >> 6)) ? wave_cnt[i] : 0u;
+    for (int i = 0; i < kSelWaves; ++i) before += (i < w) ? wave_cnt[i] : 0u;
     uint32_t pos = before + incl - mine;
     for (int i = w0; i < w1; ++i) {
       uint32_t wv = sel[i];
@@ -513,8 +590,8 @@ size_t index_select_workspace_bytes(int64_t T, int64_t S) {
   size_t b = 0;
   auto add = [&](size_t x) { b += (x + 255) / 256 * 256; };
   add((size_t)T * 4);                       // tau
-  add((size_t)T * kSeg * kCap * 8);         // survivors
-  add((size_t)T * kSeg * 4);                // counts
+  add((size_t)T * kSets * kSeg * kSegStride * 8 + kChunk * 8);  // survivors (+ copy overrun pad)
+  add((size_t)T * kSets * kSeg * 4);                // counts
   add((size_t)(T + 1) * 4);                 // fallback queue
   add((size_t)kFbBlocks * S * 4);           // fallback score rows
   return b;
@@ -533,24 +610,23 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
     return q;
   };
   float* tau = (float*)take((size_t)T * 4);
-  uint2* cand = (uint2*)take((size_t)T * kSeg * kCap * 8);
-  int32_t* cnt = (int32_t*)take((size_t)T * kSeg * 4);
+  uint2* cand = (uint2*)take((size_t)T * kSets * kSeg * kSegStride * 8 + kChunk * 8);
+  int32_t* cnt = (int32_t*)take((size_t)T * kSets * kSeg * 4);
   int32_t* fb = (int32_t*)take((size_t)(T + 1) * 4);
   float* scratch = (float*)take((size_t)kFbBlocks * S * 4);
   zero_i32_kernel<<<1, 64, 0, st>>>(fb, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  idx_estimate_kernel<<<(unsigned)((T + 15) / 16), 256, 0, st>>>(qf, qs, k8, ks, T, S, topk, tau);
+  idx_estimate_kernel<<<(unsigned)((T + 15) / 16), kEstWaves * 64, 0, st>>>(qf, qs, k8, ks, T, S, topk, tau);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  idx_filter_kernel<<<(unsigned)((T + kFiltRows - 1) / kFiltRows), 256, 0, st>>>(qf, qs, k8, ks, T, S, tau, cand,
-                                                                                  cnt);
+  idx_filter_kernel<<<(unsigned)filter_items(T), 256, 0, st>>>(qf, qs, k8, ks, T, S, tau, cand, cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nwords = (int)((S + 31) / 32);
-  const size_t lds = (size_t)2 * kSeg * kCap * 4 + (size_t)2 * nwords * 4;
+  const size_t lds = (size_t)2 * kSelMax * 4 + (size_t)nwords * 4;
   static bool attr = false;
   if (!attr) {
     e = hipFuncSetAttribute((const void*)idx_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(2 * kSeg * kCap * 4 + 2 * (262144 / 32) * 4));
+                            (int)(2 * kSelMax * 4 + (262144 / 32) * 4));
     if (e != hipSuccess) return e;
     attr = true;
   }

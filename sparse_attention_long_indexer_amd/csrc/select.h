@@ -11,7 +11,7 @@ constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr uint32_t kZeroKey = 0x80000000u;  // score_key(+0.0f)
 
 struct TopkShared {
-  uint32_t hist[256];
+  uint32_t hist[1024];
   uint32_t wave_cnt[kTopkWaves];
   uint32_t sel[2];
 };
@@ -39,68 +39,123 @@ __device__ __forceinline__ uint32_t block_prefix(bool pred, uint32_t* wave_cnt, 
 // Exact top-k of one row p[0..n) by (score desc, index asc), written in
 // ascending index order to o[0..k) with -1 padding.  All kTopkThreads
 // threads of the block call it; `sh` is block-shared scratch.
+// Block-wide exact selection of the m-th largest 32-bit key among n keys
+// (key_at(i) for i < n) that are >= lo, given every key is <= hi and at
+// least m keys are >= lo.  Radix over d = key - lo with 10-bit digits, so
+// the first digit spans only the occupied range [lo, hi].  Histogram updates
+// peel the wave's most common bin (one atomic for all its lanes) before the
+// per-lane atomics, which keeps heavy ties (ReLU zeros) cheap.
+// Returns thr (the m-th largest key) and need (how many keys equal to thr
+// belong to the top m).  hist must hold 1024 words; scan holds NT/64 words.
+template <int NT, class KeyAt>
+__device__ inline void radix_select(KeyAt key_at, int64_t n, uint32_t m, uint32_t lo, uint32_t hi,
+                                    uint32_t* hist, uint32_t* scan, uint32_t* s_out, uint32_t& thr,
+                                    uint32_t& need) {
+  constexpr int NW = NT / 64;
+  constexpr int BINS = 1024, PER = BINS / NT > 0 ? BINS / NT : 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t span = hi - lo;
+  int top = span ? 31 - __builtin_clz(span) : 0;      // highest set bit of the span
+  uint32_t prefix = 0, pmask = 0, remaining = m;
+  for (int shift = top - 9; ; shift -= 10) {
+    const int sh = shift > 0 ? shift : 0;
+    const uint32_t dmask = shift >= 0 ? 1023u : (1023u >> (-shift));
+    for (int i = tid; i < BINS; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int64_t b = 0; b < n; b += NT) {
+      const int64_t i = b + tid;
+      bool in = false;
+      uint32_t bin = 0;
+      if (i < n) {
+        const uint32_t key = key_at(i);
+        if (key >= lo) {
+          const uint32_t d = key - lo;
+          in = (d & pmask) == prefix;
+          bin = (d >> sh) & dmask;
+        }
+      }
+      // peel the most common bin of this wave: first active lane's bin
+      const uint64_t act = ballot(in);
+      if (act) {
+        const int first = __builtin_ctzll(act);
+        const uint32_t b0 = __shfl(bin, first);
+        const uint64_t same = ballot(in && bin == b0);
+        if (lane == first) atomicAdd(&hist[b0], (uint32_t)__popcll(same));
+        if (in && bin != b0) atomicAdd(&hist[bin], 1u);
+      }
+    }
+    __syncthreads();
+    // bins in descending order: thread tid owns bins BINS-1-PER*tid .. -PER+1
+    uint32_t own = 0, c[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int bi = BINS - 1 - PER * tid - e;
+      c[e] = bi >= 0 ? hist[bi] : 0u;
+      own += c[e];
+    }
+    uint32_t incl = own;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) scan[w] = incl;
+    __syncthreads();
+    uint32_t above = incl - own;
+    for (int i = 0; i < w; ++i) above += scan[i];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (above < remaining && remaining <= above + c[e]) {
+        s_out[0] = (uint32_t)(BINS - 1 - PER * tid - e);
+        s_out[1] = above;
+      }
+      above += c[e];
+    }
+    __syncthreads();
+    const uint32_t dig = s_out[0];
+    remaining -= s_out[1];
+    prefix |= dig << sh;
+    pmask |= dmask << sh;
+    __syncthreads();
+    if (shift <= 0) break;
+  }
+  thr = lo + prefix;
+  need = remaining;
+}
+
 __device__ inline void select_row(const float* __restrict__ p, int64_t n, int64_t k, int32_t* __restrict__ o,
-                           TopkShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63;
+                                  TopkShared& sh) {
+  const int tid = threadIdx.x;
   const int64_t m = n < k ? n : k;
   if (n <= k) {  // every key is kept
     for (int64_t i = tid; i < k; i += kTopkThreads) o[i] = i < n ? (int32_t)i : -1;
     return;
   }
-  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)m;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kTopkThreads) sh.hist[i] = 0;
-    __syncthreads();
-    const uint32_t zdig = (kZeroKey >> shift) & 255u;
-    for (int64_t base = 0; base < n; base += kTopkThreads) {
-      const int64_t i = base + tid;
-      uint32_t key = 0;
-      bool in = false;
-      if (i < n) {
-        key = score_key(p[i]);
-        in = (key & mask) == prefix;
-      }
-      const bool z = in && key == kZeroKey;
-      const uint64_t zb = ballot(z);
-      if (in && !z) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
-      if (zb && lane == 0) atomicAdd(&sh.hist[zdig], (uint32_t)__popcll(zb));
-    }
-    __syncthreads();
-    // find the digit holding the remaining-th largest element (wave 0)
-    if (tid < 64) {
-      // lane handles digits 255-4*lane .. 252-4*lane (descending)
-      uint32_t c4[4], sum = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c4[e] = sh.hist[255 - 4 * tid - e];
-        sum += c4[e];
-      }
-      uint32_t incl = sum;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off);
-        if (tid >= off) incl += v;
-      }
-      uint32_t above = incl - sum;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (above < remaining && remaining <= above + c4[e]) {
-          sh.sel[0] = 255u - 4u * tid - e;
-          sh.sel[1] = above;
-        }
-        above += c4[e];
-      }
-    }
-    __syncthreads();
-    const uint32_t dig = sh.sel[0];
-    remaining -= sh.sel[1];
-    prefix |= dig << shift;
-    mask |= 255u << shift;
-    __syncthreads();
+  // key range of the row
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int64_t i = tid; i < n; i += kTopkThreads) {
+    const uint32_t key = score_key(p[i]);
+    mn = min(mn, key);
+    mx = max(mx, key);
   }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) {
+    sh.wave_cnt[tid >> 6] = mn;
+    sh.hist[tid >> 6] = mx;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+  for (int i = 0; i < kTopkWaves; ++i) {
+    mn = min(mn, sh.wave_cnt[i]);
+    mx = max(mx, sh.hist[i]);
+  }
+  __syncthreads();
+  uint32_t thr, need;
+  radix_select<kTopkThreads>([&](int64_t i) { return score_key(p[i]); }, n, (uint32_t)m, mn, mx, sh.hist,
+                             sh.wave_cnt, sh.sel, thr, need);
 
-  // ordered selection: keys > prefix, and the first `remaining` keys == prefix
-  const uint32_t thr = prefix, need = remaining;
+  // ordered selection: keys > thr, and the first `need` keys == thr
   uint32_t carry_eq = 0, carry_sel = 0;
   for (int64_t base = 0; base < n && carry_sel < (uint32_t)m; base += kTopkThreads) {
     const int64_t i = base + tid;
@@ -118,6 +173,5 @@ __device__ inline void select_row(const float* __restrict__ p, int64_t n, int64_
   }
   for (int64_t i = m + tid; i < k; i += kTopkThreads) o[i] = -1;
 }
-
 
 }  // namespace dsa
