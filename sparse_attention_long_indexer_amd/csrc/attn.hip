@@ -19,6 +19,7 @@
 // fp32 path: a plain VALU kernel for the small fp32 configuration.
 #include "common.h"
 #include "kernels.h"
+#include "dsa.h"
 
 namespace dsa {
 
@@ -66,11 +67,17 @@ __device__ __forceinline__ int valid_count(const int32_t* ip, int64_t k, int* s_
 }
 
 // LDS tile of NK gathered rows, each row C chunks of 16 bytes.  Chunk X of
-// row r lives at slot r*C + (X ^ ((r >> 1) & 7)): 16 consecutive rows read at
-// the same logical chunk hit 16 distinct 4-bank groups.
+// row r lives at slot r*C + (X ^ swz(r)), swz(r) = 2*((r>>1)&3) + ((r>>3)&1):
+//  - 16 consecutive rows read at one logical chunk (the K fragments) hit 16
+//    distinct 4-bank groups (r&1 picks the half, swz the group), and
+//  - the transposed V reads (4 rows x 2 adjacent chunks per 16 lanes, rows
+//    4G.. of two lane groups per 256 bytes) also land on distinct groups,
+//    since rows r and r+2 differ in bits 1-2 of swz.
+// Rows r and r+16 share swz.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 template <int C>
 __device__ __forceinline__ int tile_slot(int r, int X) {
-  return r * C + (X ^ ((r >> 1) & 7));
+  return r * C + (X ^ swz(r));
 }
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -85,11 +92,12 @@ __device__ __forceinline__ v4s lds_read_tr16(const char* lds_base, int byte_off)
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)((lds_char*)lds_base + byte_off));
 }
 
-template <int DK, int DV, int HW, int NW, bool SEPV>
+template <int DK, int DV, int HW, int NW, bool SEPV, int NBUF>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const int64_t* seq_off) {
   constexpr int NK = 32;                        // keys per tile
   constexpr int KC = DK / 8;                    // 16-byte chunks per K row
   constexpr int VC = SEPV ? DV / 8 : 0;         // chunks per separate V row
+  constexpr int VCH = SEPV ? VC : KC;           // chunks per row of the V rows
   constexpr int TILE_CHUNKS = NK * (KC + VC);
   constexpr int NT = NW * 64;
   constexpr int LOADS = (TILE_CHUNKS + NT - 1) / NT;  // 16-byte gathers per lane per tile
@@ -98,58 +106,56 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   constexpr int TILE_BYTES = TILE_CHUNKS * 16;
   static_assert((NK * KC) % 64 == 0, "K region must be whole wave loads");
   static_assert(KC % 8 == 0 && VC % 8 == 0, "swizzle works on groups of 8 chunks");
-  extern __shared__ __align__(16) char smem[];  // [2][TILE_BYTES]
+  extern __shared__ __align__(16) char smem[];  // [NBUF][TILE_BYTES] tiles, then the index row
+  int32_t* sidx = (int32_t*)(smem + NBUF * TILE_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int64_t t = blockIdx.x;
   __shared__ int s_cnt;
   const AttnRow row = attn_row(a, seq_off, t);
-  const int n = valid_count(row.ip, a.k, &s_cnt);
+  // stage the query's index row; n = leading valid entries
+  if (tid == 0) s_cnt = (int)a.k;
+  __syncthreads();
+  {
+    int first = (int)a.k;
+    for (int j = tid; j < (int)a.k; j += NT) {
+      int32_t s = row.ip[j];
+      if (s < 0 && j < first) first = j;
+      sidx[j] = s < row.len ? s : (int32_t)(row.len - 1);
+    }
+    if (first < (int)a.k) atomicMin(&s_cnt, first);
+  }
+  __syncthreads();
+  const int n = s_cnt;
   const char* kvb = (const char*)a.kv;
   const char* vvb = SEPV ? (const char*)a.v : kvb;
   const int64_t ldk = a.ld_kv * 2, ldv = (SEPV ? a.ld_v : a.ld_kv) * 2;  // bytes
 
-  // gather plan: load i of wave w fills slots (i*NW + w)*64 + lane; a wave
-  // whose slot range lies past the tile skips that load (wave-uniform)
-  auto slot_row = [&](int i, int& r, int& off, bool& isv) {
-    const int slot = (i * NW + w) * 64 + lane;
-    isv = VC > 0 && slot >= NK * KC;
-    const int rs = isv ? slot - NK * KC : slot;
-    const int CC = isv ? (VC > 0 ? VC : 8) : KC;
-    r = rs / CC;
-    const int pc = rs - r * CC;
-    off = (pc ^ ((r >> 1) & 7)) * 16;   // logical chunk stored at this slot, in bytes
-  };
-  auto fetch_idx = [&](int j0, int32_t* keys) {
+  // gather: load i of wave w fills slots (i*NW + w)*64 + lane of the tile; a
+  // wave whose slot range lies past the tile skips that load (wave-uniform)
+  auto issue_tile = [&](int tile) {
+    const int j0 = tile * NK;
+    char* dst = smem + (tile % NBUF) * TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       if ((i * NW + w) * 64 >= TILE_CHUNKS) break;
-      int r, off;
-      bool isv;
-      slot_row(i, r, off, isv);
+      const int slot = (i * NW + w) * 64 + lane;
+      const bool isv = VC > 0 && slot >= NK * KC;
+      const int rs = isv ? slot - NK * KC : slot;
+      const int CC = isv ? (VC > 0 ? VC : 8) : KC;
+      const int r = rs / CC;
+      const int off = ((rs - r * CC) ^ swz(r)) * 16;  // logical chunk stored at this slot
       const int j = j0 + r;
-      int32_t s = row.ip[j < n ? j : j0];
-      keys[i] = s < row.len ? s : (int32_t)(row.len - 1);
-    }
-  };
-  auto issue_tile = [&](int buf, const int32_t* keys) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      if ((i * NW + w) * 64 >= TILE_CHUNKS) break;
-      int r, off;
-      bool isv;
-      slot_row(i, r, off, isv);
-      const int64_t kr = row.base + keys[i];
+      const int64_t kr = row.base + sidx[j < n ? j : j0];
       const char* src = isv ? vvb + kr * ldv + off : kvb + kr * ldk + off;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (__attribute__((address_space(3))) void*)((lds_char*)smem + buf * TILE_BYTES + (i * NW + w) * 1024),
-          16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)((lds_char*)dst + (i * NW + w) * 1024),
+                                       16, 0, 0);
     }
   };
 
-  // Q^T fragments: head 32w.. (HW per wave), subtile hs: head HW*w + 16hs + c
+  // Q^T fragments: subtile hs holds head HW*w + 16hs + c, dims 32kk + 8g .. +8
   v8s qf[HS][DK / 32];
 #pragma unroll
   for (int hs = 0; hs < HS; ++hs) {
@@ -170,40 +176,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   }
   const float zs = a.scale * kLog2e;
   const int ntiles = (n + NK - 1) / NK;
-  constexpr int VCH = SEPV ? VC : KC;  // chunks per row of the V rows
+  // K rows c and 16 + c share a swizzle: chunk 4kk + g of row c sits at
+  // 8*(kk/2) + ((4*(kk%2) + g) ^ sw(c)).  V^T reads use rows r0 = 4G + sl/4
+  // and r0 + 16; dv chunk 2d + (sl%4)/2 sits at 8*(d/4) + ((2*(d%4) +
+  // (sl%4)/2) ^ sw(r0)).
   int kbase[2], vbase[4];
   {
-    const int sw = (c >> 1) & 7;
+    const int sw = swz(c);
     kbase[0] = (c * KC + (g ^ sw)) * 16;
     kbase[1] = (c * KC + ((4 + g) ^ sw)) * 16;
     const int sl = lane & 15, G = lane >> 4;
-    const int r0 = 4 * G + (sl >> 2), swv = (r0 >> 1) & 7;
+    const int r0 = 4 * G + (sl >> 2), swv = swz(r0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) vbase[q] = (r0 * VCH + ((2 * q + ((sl & 3) >> 1)) ^ swv)) * 16 + (sl & 1) * 8;
   }
 
-  int32_t keys[LOADS];
-  if (ntiles > 0) {
-    fetch_idx(0, keys);
-    issue_tile(0, keys);
-    if (ntiles > 1) fetch_idx(NK, keys);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int j0 = it * NK;
-    if (it + 1 < ntiles) {
-      issue_tile((it + 1) & 1, keys);
-      if (it + 2 < ntiles) fetch_idx(j0 + 2 * NK, keys);
-    }
-    const char* tb = smem + (it & 1) * TILE_BYTES;
-
-    // S^T = K . Q^T : key subtiles ks (rows 16ks + c), head subtiles hs.
-    // Chunk 4kk + g of row r sits at 8*(kk/2) + ((4*(kk%2) + g) ^ sw(r)), and
-    // rows c and 16 + c share sw, so two base offsets plus immediates cover
-    // every read.
-    v4f sacc[2][HS];
+  // S^T = K . Q^T for one tile (key subtiles ks = rows 16ks + c)
+  auto qk = [&](int tile, v4f (&sacc)[2][HS]) {
+    const char* tb = smem + (tile % NBUF) * TILE_BYTES;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -218,58 +208,47 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       }
       if (kk % DSA_QK_GROUP == DSA_QK_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
     }
-
-    // online softmax (log2 domain); the running max only moves when a tile
-    // raises it by more than 2^8, so O is rescaled rarely
-    v8s pb[HS];
+  };
+  // online softmax of one tile (log2 domain).  The running max only moves
+  // when a tile raises it by more than 2^8, so O is rescaled rarely; returns
+  // whether any lane needs the rescale, with the factor in corr.
+  auto softmax = [&](int tile, const v4f (&sacc)[2][HS], v8s (&pb)[HS], float (&corr)[HS]) -> bool {
+    const int j0 = tile * NK;
     bool need_any = false;
-    float zt[HS][8], mnew[HS];
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
+      float zt[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        zt[hs][i] = (j0 + 4 * g + i < n) ? sacc[0][hs][i] * zs : -INFINITY;
-        zt[hs][4 + i] = (j0 + 16 + 4 * g + i < n) ? sacc[1][hs][i] * zs : -INFINITY;
+        zt[i] = (j0 + 4 * g + i < n) ? sacc[0][hs][i] * zs : -INFINITY;
+        zt[4 + i] = (j0 + 16 + 4 * g + i < n) ? sacc[1][hs][i] * zs : -INFINITY;
       }
-      float mx = zt[hs][0];
+      float mx = zt[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, zt[hs][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, zt[i]);
+      mx = rows_max(mx);
       const bool need = mx > m_run[hs] + 8.f;
-      mnew[hs] = need ? mx : m_run[hs];
+      const float mnew = need ? mx : m_run[hs];
+      corr[hs] = exp2f(m_run[hs] - mnew);
       need_any |= need;
-    }
-    if (__any(need_any)) {
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) {
-        const float corr = exp2f(m_run[hs] - mnew[hs]);
-        l_part[hs] *= corr;
-#pragma unroll
-        for (int d = 0; d < DV / 16; ++d) o[d][hs] *= corr;
-        m_run[hs] = mnew[hs];
-      }
-    }
-#pragma unroll
-    for (int hs = 0; hs < HS; ++hs) {
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = exp2f(zt[hs][i] - m_run[hs]);
-        l_part[hs] += p[i];
-      }
+      m_run[hs] = mnew;
+      float ps = 0.f;
       v4i pk;
-      pk[0] = (int)pack_bf16x2(p[0], p[1]);
-      pk[1] = (int)pack_bf16x2(p[2], p[3]);
-      pk[2] = (int)pack_bf16x2(p[4], p[5]);
-      pk[3] = (int)pack_bf16x2(p[6], p[7]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = exp2f(zt[2 * i] - mnew), p1 = exp2f(zt[2 * i + 1] - mnew);
+        ps += p0 + p1;
+        pk[i] = (int)pack_bf16x2(p0, p1);
+      }
+      l_part[hs] = l_part[hs] * corr[hs] + ps;
       pb[hs] = (v8s)pk;
     }
-
-    // O^T += V^T . P^T ; V^T fragment via two transposed reads (rows
-    // r0 = 4G + sl/4 and r0 + 16, which share a swizzle), dv chunk
-    // 2d + (sl%4)/2 at 8*(d/4) + ((2*(d%4) + (sl%4)/2) ^ sw(r0))
-    const char* vb = SEPV ? tb + NK * KC * 16 : tb;
+    return __any(need_any);
+  };
+  // O^T += V^T . P^T for one tile; V^T fragment via two transposed reads
+  auto pv = [&](int tile, const v8s (&pb)[HS]) {
+    const char* tp = smem + (tile % NBUF) * TILE_BYTES;
+    const char* vb = SEPV ? tp + NK * KC * 16 : tp;
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
       const int off = vbase[d & 3] + (d >> 2) * 128;
@@ -280,17 +259,53 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       for (int hs = 0; hs < HS; ++hs) o[d][hs] = mfma_bf16_16x16x32(av, pb[hs], o[d][hs]);
       if (d % DSA_PV_GROUP == DSA_PV_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto rescale = [&](const float (&corr)[HS]) {
+#pragma unroll
+    for (int hs = 0; hs < HS; ++hs)
+#pragma unroll
+      for (int d = 0; d < DV / 16; ++d) o[d][hs] *= corr[hs];
+  };
 
+  // Pipeline over tiles: step it gathers tile it+1, computes S^T of tile it,
+  // then runs the PV MFMAs of tile it-1 while the VALU does tile it's
+  // softmax.  With three LDS buffers one barrier per step suffices; with two
+  // (large separate-V tiles) the gather of tile it+1 waits for PV of it-1.
+  if (ntiles > 0) {
+    issue_tile(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    v4f sacc[2][HS];
+    v8s pb[HS];
+    float corr[HS];
+    if (ntiles > 1) issue_tile(1);  // buffer 1 is free in either scheme
+    qk(0, sacc);
+    softmax(0, sacc, pb, corr);  // O is still zero: no rescale needed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int it = 1; it < ntiles; ++it) {
+      if (NBUF >= 3 && it + 1 < ntiles) issue_tile(it + 1);
+      qk(it, sacc);
+      v8s pbn[HS];
+      const bool rs = softmax(it, sacc, pbn, corr);
+      pv(it - 1, pb);
+      if (rs) rescale(corr);
+      if (NBUF == 2 && it + 1 < ntiles) {
+        __syncthreads();
+        issue_tile(it + 1);
+      }
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) pb[hs] = pbn[hs];
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    pv(ntiles - 1, pb);
   }
 
   // epilogue: lane (c, g) holds O^T[dv = 16d + 4g + i][head HW*w + 16hs + c]
 #pragma unroll
   for (int hs = 0; hs < HS; ++hs) {
-    float l = l_part[hs];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = rows_sum(l_part[hs]);
     const int h = HW * w + 16 * hs + c;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV;
@@ -399,15 +414,18 @@ size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t 
 
 template <int DK, int DV, int HW, int NW, bool SEPV>
 static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
-  constexpr size_t lds = 2 * (size_t)32 * (DK / 8 + (SEPV ? DV / 8 : 0)) * 16;
+  constexpr size_t tile = (size_t)32 * (DK / 8 + (SEPV ? DV / 8 : 0)) * 16;
+  constexpr int NBUF = 3 * tile + (size_t)DSA_MAX_TOPK * 4 <= 160 * 1024 ? 3 : 2;
+  constexpr size_t lds_max = NBUF * tile + (size_t)DSA_MAX_TOPK * 4;
+  const size_t lds = NBUF * tile + (size_t)a.k * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<DK, DV, HW, NW, SEPV>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<DK, DV, HW, NW, SEPV, NBUF>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attn_bf16_kernel<DK, DV, HW, NW, SEPV><<<(unsigned)a.T, NW * 64, lds, st>>>(a, seq_off);
+  attn_bf16_kernel<DK, DV, HW, NW, SEPV, NBUF><<<(unsigned)a.T, NW * 64, lds, st>>>(a, seq_off);
   return hipGetLastError();
 }
 
