@@ -38,28 +38,29 @@ def hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    lang = ["-x", "hip"]
+    extra = os.environ.get("DSA_EXTRA_HIPCC_FLAGS", "").split()   # tuning experiments only
+    cmd = [hipcc()] + FLAGS + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libdsa.so; returns its path."""
+def build(verbose: bool = False, out: str = LIB) -> str:
+    """Compile every source and link libdsa.so (or `out`); returns its path."""
     with tempfile.TemporaryDirectory(prefix="dsa_build_") as tmp:
         objs = [os.path.join(tmp, s.replace(".", "_") + ".o") for s in SOURCES]
         with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
             list(ex.map(_compile, SOURCES, objs))
-        out_tmp = LIB + ".tmp"
+        out_tmp = out + ".tmp"
         cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", out_tmp] + objs
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-        os.replace(out_tmp, LIB)
+        os.replace(out_tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

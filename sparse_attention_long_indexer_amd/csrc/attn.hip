@@ -66,20 +66,13 @@ __device__ __forceinline__ int valid_count(const int32_t* ip, int64_t k, int* s_
   return *s_cnt;
 }
 
-// LDS tile of NK gathered rows, each row C chunks of 16 bytes.  Chunk X of
-// row r lives at slot r*C + (X ^ swz(r)), swz(r) = 2*((r>>1)&3) + ((r>>3)&1):
-//  - 16 consecutive rows read at one logical chunk (the K fragments) hit 16
-//    distinct 4-bank groups (r&1 picks the half, swz the group), and
-//  - the transposed V reads (4 rows x 2 adjacent chunks per 16 lanes, rows
-//    4G.. of two lane groups per 256 bytes) also land on distinct groups,
-//    since rows r and r+2 differ in bits 1-2 of swz.
-// Rows r and r+16 share swz.
-__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
-template <int C>
-__device__ __forceinline__ int tile_slot(int r, int X) {
-  return r * C + (X ^ swz(r));
-}
-
+// LDS tile of NK = 32 gathered rows, stored fragment-major: the rows form
+// two 16-row key subtiles, each row C chunks of 16 bytes; fragment
+// (ks, q) holds chunks 4q .. 4q+3 of rows 16ks .. 16ks+15 as 64 slots
+// (chunk-column major, slot = 16 * (X % 4) + row % 16).  One 16x16x32 MFMA
+// operand is then one lane-linear 1 KB read, and a transposed V read (4 rows
+// x 2 adjacent chunks per 16 lanes) covers two contiguous 256-byte runs.
+// Each gathered fragment is one 64-lane direct-to-LDS copy.
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -100,16 +93,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   constexpr int VCH = SEPV ? VC : KC;           // chunks per row of the V rows
   constexpr int TILE_CHUNKS = NK * (KC + VC);
   constexpr int NT = NW * 64;
-  constexpr int LOADS = (TILE_CHUNKS + NT - 1) / NT;  // 16-byte gathers per lane per tile
+  constexpr int LOADS = (TILE_CHUNKS / 64 + NW - 1) / NW;  // fragment copies per wave per tile
   constexpr int HS = HW / 16;                   // 16-head subtiles per wave
   constexpr int H = HW * NW;
   constexpr int TILE_BYTES = TILE_CHUNKS * 16;
-  static_assert((NK * KC) % 64 == 0, "K region must be whole wave loads");
-  static_assert(KC % 8 == 0 && VC % 8 == 0, "swizzle works on groups of 8 chunks");
+  static_assert(KC % 4 == 0 && VC % 4 == 0, "fragments are 4 chunks wide");
+  constexpr int KF = 2 * (KC / 4);              // K fragments per tile
+  constexpr int NFRAG = KF + 2 * (VC / 4);      // fragments per tile
   extern __shared__ __align__(16) char smem[];  // [NBUF][TILE_BYTES] tiles, then the index row
   int32_t* sidx = (int32_t*)(smem + NBUF * TILE_BYTES);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const int64_t t = blockIdx.x;
   __shared__ int s_cnt;
@@ -132,26 +127,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   const char* vvb = SEPV ? (const char*)a.v : kvb;
   const int64_t ldk = a.ld_kv * 2, ldv = (SEPV ? a.ld_v : a.ld_kv) * 2;  // bytes
 
-  // gather: load i of wave w fills slots (i*NW + w)*64 + lane of the tile; a
-  // wave whose slot range lies past the tile skips that load (wave-uniform)
+  // gather: copy i of wave w fills fragment f = i*NW + w of the tile; lane
+  // l brings chunk 4q + l/16 of row 16ks + l%16 (a wave past the last
+  // fragment skips the copy, wave-uniform)
   auto issue_tile = [&](int tile) {
     const int j0 = tile * NK;
     char* dst = smem + (tile % NBUF) * TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      if ((i * NW + w) * 64 >= TILE_CHUNKS) break;
-      const int slot = (i * NW + w) * 64 + lane;
-      const bool isv = VC > 0 && slot >= NK * KC;
-      const int rs = isv ? slot - NK * KC : slot;
-      const int CC = isv ? (VC > 0 ? VC : 8) : KC;
-      const int r = rs / CC;
-      const int off = ((rs - r * CC) ^ swz(r)) * 16;  // logical chunk stored at this slot
+      const int f = i * NW + w;
+      if (f >= NFRAG) break;
+      const bool isv = VC > 0 && f >= KF;
+      const int fr = isv ? f - KF : f;
+      const int FQ = isv ? (VC > 0 ? VC / 4 : 1) : KC / 4;
+      const int ks = fr / FQ, q = fr - ks * FQ;
+      const int r = 16 * ks + (lane & 15);
+      const int off = (4 * q + (lane >> 4)) * 16;
       const int j = j0 + r;
       const int64_t kr = row.base + sidx[j < n ? j : j0];
       const char* src = isv ? vvb + kr * ldv + off : kvb + kr * ldk + off;
       __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)((lds_char*)dst + (i * NW + w) * 1024),
-                                       16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)((lds_char*)dst + f * 1024), 16, 0,
+                                       0);
     }
   };
 
@@ -176,20 +173,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   }
   const float zs = a.scale * kLog2e;
   const int ntiles = (n + NK - 1) / NK;
-  // K rows c and 16 + c share a swizzle: chunk 4kk + g of row c sits at
-  // 8*(kk/2) + ((4*(kk%2) + g) ^ sw(c)).  V^T reads use rows r0 = 4G + sl/4
-  // and r0 + 16; dv chunk 2d + (sl%4)/2 sits at 8*(d/4) + ((2*(d%4) +
-  // (sl%4)/2) ^ sw(r0)).
-  int kbase[2], vbase[4];
-  {
-    const int sw = swz(c);
-    kbase[0] = (c * KC + (g ^ sw)) * 16;
-    kbase[1] = (c * KC + ((4 + g) ^ sw)) * 16;
-    const int sl = lane & 15, G = lane >> 4;
-    const int r0 = 4 * G + (sl >> 2), swv = swz(r0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) vbase[q] = (r0 * VCH + ((2 * q + ((sl & 3) >> 1)) ^ swv)) * 16 + (sl & 1) * 8;
-  }
+  // V^T reads: lane (sl, G) reads row 4G + sl/4 (+16h), dv 16d + 4(sl%4):
+  // chunk X = 2d + (sl%4)/2, half sl%2, i.e. slot
+  // ((h*VF + d/2)*4 + 2(d%2) + (sl%4)/2)*16 + 4G + sl/4 with VF = VCH/4.
+  const int vbase = ((((lane & 3) >> 1) * 16) + 4 * (lane >> 4) + ((lane & 15) >> 2)) * 16 + (lane & 1) * 8;
+  constexpr int VF = VCH / 4;
 
   // S^T = K . Q^T for one tile (key subtiles ks = rows 16ks + c)
   auto qk = [&](int tile, v4f (&sacc)[2][HS]) {
@@ -202,7 +190,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     for (int kk = 0; kk < DK / 32; ++kk) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const v8s kf = *(const v8s*)(tb + kbase[kk & 1] + ks * (16 * KC * 16) + (kk >> 1) * 128);
+        const v8s kf = *(const v8s*)(tb + ((ks * (KC / 4) + kk) * 64 + lane) * 16);
 #pragma unroll
         for (int hs = 0; hs < HS; ++hs) sacc[ks][hs] = mfma_bf16_16x16x32(kf, qf[hs][kk], sacc[ks][hs]);
       }
@@ -248,12 +236,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   // O^T += V^T . P^T for one tile; V^T fragment via two transposed reads
   auto pv = [&](int tile, const v8s (&pb)[HS]) {
     const char* tp = smem + (tile % NBUF) * TILE_BYTES;
-    const char* vb = SEPV ? tp + NK * KC * 16 : tp;
+    const char* vb = SEPV ? tp + KF * 1024 : tp;
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
-      const int off = vbase[d & 3] + (d >> 2) * 128;
+      const int off = vbase + ((d >> 1) * 4 + 2 * (d & 1)) * 256;
       const v4s lo = lds_read_tr16(vb, off);
-      const v4s hi = lds_read_tr16(vb, off + 16 * VCH * 16);
+      const v4s hi = lds_read_tr16(vb, off + VF * 1024);
       const v8s av = (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int hs = 0; hs < HS; ++hs) o[d][hs] = mfma_bf16_16x16x32(av, pb[hs], o[d][hs]);
@@ -267,39 +255,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       for (int d = 0; d < DV / 16; ++d) o[d][hs] *= corr[hs];
   };
 
-  // Pipeline over tiles: step it gathers tile it+1, computes S^T of tile it,
-  // then runs the PV MFMAs of tile it-1 while the VALU does tile it's
-  // softmax.  With three LDS buffers one barrier per step suffices; with two
-  // (large separate-V tiles) the gather of tile it+1 waits for PV of it-1.
+  // Per tile: S^T, softmax, PV.  The gather of tile it+1 is issued before
+  // tile it's math into the other buffer, which every wave finished reading
+  // before the barrier that closed the previous step.
   if (ntiles > 0) {
     issue_tile(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    v4f sacc[2][HS];
-    v8s pb[HS];
-    float corr[HS];
-    if (ntiles > 1) issue_tile(1);  // buffer 1 is free in either scheme
-    qk(0, sacc);
-    softmax(0, sacc, pb, corr);  // O is still zero: no rescale needed
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int it = 1; it < ntiles; ++it) {
-      if (NBUF >= 3 && it + 1 < ntiles) issue_tile(it + 1);
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + 1 < ntiles) issue_tile(it + 1);
+      v4f sacc[2][HS];
       qk(it, sacc);
-      v8s pbn[HS];
-      const bool rs = softmax(it, sacc, pbn, corr);
-      pv(it - 1, pb);
-      if (rs) rescale(corr);
-      if (NBUF == 2 && it + 1 < ntiles) {
-        __syncthreads();
-        issue_tile(it + 1);
-      }
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) pb[hs] = pbn[hs];
+      v8s pb[HS];
+      float corr[HS];
+      if (softmax(it, sacc, pb, corr)) rescale(corr);
+      pv(it, pb);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    pv(ntiles - 1, pb);
   }
 
   // epilogue: lane (c, g) holds O^T[dv = 16d + 4g + i][head HW*w + 16hs + c]
@@ -415,7 +388,7 @@ size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t 
 template <int DK, int DV, int HW, int NW, bool SEPV>
 static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
   constexpr size_t tile = (size_t)32 * (DK / 8 + (SEPV ? DV / 8 : 0)) * 16;
-  constexpr int NBUF = 3 * tile + (size_t)DSA_MAX_TOPK * 4 <= 160 * 1024 ? 3 : 2;
+  constexpr int NBUF = 2;
   constexpr size_t lds_max = NBUF * tile + (size_t)DSA_MAX_TOPK * 4;
   const size_t lds = NBUF * tile + (size_t)a.k * 4;
   static bool attr_set = false;
