@@ -21,6 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 
 SOURCES = ["fold.hip", "index_scores.hip", "topk.hip", "index_select.hip", "attn.hip", "api.cpp"]
+SOURCE_FLAGS = {}   # per-source extra hipcc flags
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -40,7 +41,7 @@ def hipcc() -> str:
 def _compile(src: str, obj: str) -> None:
     lang = ["-x", "hip"]
     extra = os.environ.get("DSA_EXTRA_HIPCC_FLAGS", "").split()   # tuning experiments only
-    cmd = [hipcc()] + FLAGS + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -77,7 +77,7 @@ dsa_status_t check_attn(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dty
   if (dt != DSA_BF16 && dt != DSA_F32) return DSA_ERR_DTYPE;
   if (T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
   if (ld_kv < Dk || (v ? ld_v < Dv : ld_kv < Dv)) return DSA_ERR_SHAPE;
-  if (!attn_supported(dt == DSA_F32, H, Dk, Dv)) return DSA_ERR_UNSUPPORTED;
+  if (!attn_supported(dt == DSA_F32, H, Dk, Dv, v != nullptr, k)) return DSA_ERR_UNSUPPORTED;
   if (T == 0) return DSA_OK;
   if (!q || !kv || !idx || !out) return DSA_ERR_NULL;
   if (dt == DSA_BF16) {

@@ -23,10 +23,6 @@
 
 namespace dsa {
 
-#ifndef DSA_MLA_HW
-#define DSA_MLA_HW 16   // heads per wave for the 128-head MLA shape
-#define DSA_MLA_NW 8    // waves per block
-#endif
 #ifndef DSA_QK_GROUP
 #define DSA_QK_GROUP 4  // QK k-steps the scheduler may interleave
 #define DSA_PV_GROUP 4  // PV dv-subtiles the scheduler may interleave
@@ -85,7 +81,7 @@ __device__ __forceinline__ v4s lds_read_tr16(const char* lds_base, int byte_off)
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)((lds_char*)lds_base + byte_off));
 }
 
-template <int DK, int DV, int HW, int NW, bool SEPV, int NBUF>
+template <int DK, int DV, int NW, bool SEPV>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const int64_t* seq_off) {
   constexpr int NK = 32;                        // keys per tile
   constexpr int KC = DK / 8;                    // 16-byte chunks per K row
@@ -93,21 +89,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   constexpr int VCH = SEPV ? VC : KC;           // chunks per row of the V rows
   constexpr int TILE_CHUNKS = NK * (KC + VC);
   constexpr int NT = NW * 64;
-  constexpr int LOADS = (TILE_CHUNKS / 64 + NW - 1) / NW;  // fragment copies per wave per tile
-  constexpr int HS = HW / 16;                   // 16-head subtiles per wave
-  constexpr int H = HW * NW;
+  constexpr int H = 16 * NW;                    // wave w owns heads 16w .. 16w+15 for QK/softmax
+  constexpr int DVW = DV / NW;                  // ... and value columns w*DVW .. +DVW for PV
+  constexpr int ND = DVW / 16;
   constexpr int TILE_BYTES = TILE_CHUNKS * 16;
   static_assert(KC % 4 == 0 && VC % 4 == 0, "fragments are 4 chunks wide");
+  static_assert(DV % (16 * NW) == 0, "value columns split evenly over the waves");
   constexpr int KF = 2 * (KC / 4);              // K fragments per tile
   constexpr int NFRAG = KF + 2 * (VC / 4);      // fragments per tile
-  extern __shared__ __align__(16) char smem[];  // [NBUF][TILE_BYTES] tiles, then the index row
-  int32_t* sidx = (int32_t*)(smem + NBUF * TILE_BYTES);
+  constexpr int LOADS = (NFRAG + NW - 1) / NW;  // fragment copies per wave per tile
+  constexpr int VF = VCH / 4;
+  // dynamic LDS: [2][TILE_BYTES] tiles | [NW] P^T fragments (1 KB) | index row
+  extern __shared__ __align__(16) char smem[];
+  char* pbuf = smem + 2 * TILE_BYTES;
+  int32_t* sidx = (int32_t*)(pbuf + NW * 1024);
+  __shared__ float s_corr[H], s_l[H];
+  __shared__ int s_need[NW];
+  __shared__ int s_cnt;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const int64_t t = blockIdx.x;
-  __shared__ int s_cnt;
   const AttnRow row = attn_row(a, seq_off, t);
   // stage the query's index row; n = leading valid entries
   if (tid == 0) s_cnt = (int)a.k;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   // fragment skips the copy, wave-uniform)
   auto issue_tile = [&](int tile) {
     const int j0 = tile * NK;
-    char* dst = smem + (tile % NBUF) * TILE_BYTES;
+    char* dst = smem + (tile & 1) * TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + w;
@@ -152,74 +155,68 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     }
   };
 
-  // Q^T fragments: subtile hs holds head HW*w + 16hs + c, dims 32kk + 8g .. +8
-  v8s qf[HS][DK / 32];
+  // Q^T fragments of head 16w + c, dims 32kk + 8g .. +8
+  v8s qf[DK / 32];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((t * H) + 16 * w + c) * (int64_t)DK + 8 * g;
 #pragma unroll
-  for (int hs = 0; hs < HS; ++hs) {
-    const uint16_t* qp = (const uint16_t*)a.q + ((t * H) + HW * w + 16 * hs + c) * (int64_t)DK + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) qf[hs][kk] = *(const v8s*)(qp + 32 * kk);
+    for (int kk = 0; kk < DK / 32; ++kk) qf[kk] = *(const v8s*)(qp + 32 * kk);
   }
-  v4f o[DV / 16][HS];
+  // O^T accumulators: value subtile d of this wave's columns x head subtile hs
+  v4f o[ND][NW];
 #pragma unroll
-  for (int d = 0; d < DV / 16; ++d)
+  for (int d = 0; d < ND; ++d)
 #pragma unroll
-    for (int hs = 0; hs < HS; ++hs) o[d][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run[HS], l_part[HS];
-#pragma unroll
-  for (int hs = 0; hs < HS; ++hs) {
-    m_run[hs] = -INFINITY;
-    l_part[hs] = 0.f;
-  }
+    for (int hs = 0; hs < NW; ++hs) o[d][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
   const float zs = a.scale * kLog2e;
   const int ntiles = (n + NK - 1) / NK;
-  // V^T reads: lane (sl, G) reads row 4G + sl/4 (+16h), dv 16d + 4(sl%4):
-  // chunk X = 2d + (sl%4)/2, half sl%2, i.e. slot
-  // ((h*VF + d/2)*4 + 2(d%2) + (sl%4)/2)*16 + 4G + sl/4 with VF = VCH/4.
+  // V^T reads: lane (sl, G) reads row 4G + sl/4 (+16h), dv 16D + 4(sl%4):
+  // chunk X = 2D + (sl%4)/2, half sl%2, i.e. slot
+  // ((h*VF + D/2)*4 + 2(D%2) + (sl%4)/2)*16 + 4G + sl/4.
   const int vbase = ((((lane & 3) >> 1) * 16) + 4 * (lane >> 4) + ((lane & 15) >> 2)) * 16 + (lane & 1) * 8;
-  constexpr int VF = VCH / 4;
 
-  // S^T = K . Q^T for one tile (key subtiles ks = rows 16ks + c)
-  auto qk = [&](int tile, v4f (&sacc)[2][HS]) {
-    const char* tb = smem + (tile % NBUF) * TILE_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) sacc[ks][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // Per tile: S^T and softmax for the wave's 16 heads, P^T published to
+  // LDS, then O^T for all heads over the wave's value columns.  The gather
+  // of tile it+1 is issued first, into the buffer every wave finished
+  // reading before the barrier that closed the previous tile.
+  if (ntiles > 0) {
+    issue_tile(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) issue_tile(it + 1);
+    const char* tb = smem + (it & 1) * TILE_BYTES;
+    const int j0 = it * NK;
+    // S^T = K . Q^T (key subtiles ks = rows 16ks + c)
+    v4f sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kk = 0; kk < DK / 32; ++kk) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const v8s kf = *(const v8s*)(tb + ((ks * (KC / 4) + kk) * 64 + lane) * 16);
-#pragma unroll
-        for (int hs = 0; hs < HS; ++hs) sacc[ks][hs] = mfma_bf16_16x16x32(kf, qf[hs][kk], sacc[ks][hs]);
+        sacc[ks] = mfma_bf16_16x16x32(kf, qf[kk], sacc[ks]);
       }
       if (kk % DSA_QK_GROUP == DSA_QK_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  // online softmax of one tile (log2 domain).  The running max only moves
-  // when a tile raises it by more than 2^8, so O is rescaled rarely; returns
-  // whether any lane needs the rescale, with the factor in corr.
-  auto softmax = [&](int tile, const v4f (&sacc)[2][HS], v8s (&pb)[HS], float (&corr)[HS]) -> bool {
-    const int j0 = tile * NK;
-    bool need_any = false;
-#pragma unroll
-    for (int hs = 0; hs < HS; ++hs) {
+    // online softmax (log2 domain); the running max only moves when a tile
+    // raises it by more than 2^8, so O is rescaled rarely
+    {
       float zt[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        zt[i] = (j0 + 4 * g + i < n) ? sacc[0][hs][i] * zs : -INFINITY;
-        zt[4 + i] = (j0 + 16 + 4 * g + i < n) ? sacc[1][hs][i] * zs : -INFINITY;
+        zt[i] = (j0 + 4 * g + i < n) ? sacc[0][i] * zs : -INFINITY;
+        zt[4 + i] = (j0 + 16 + 4 * g + i < n) ? sacc[1][i] * zs : -INFINITY;
       }
       float mx = zt[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, zt[i]);
       mx = rows_max(mx);
-      const bool need = mx > m_run[hs] + 8.f;
-      const float mnew = need ? mx : m_run[hs];
-      corr[hs] = exp2f(m_run[hs] - mnew);
-      need_any |= need;
-      m_run[hs] = mnew;
+      const bool need = mx > m_run + 8.f;
+      const float mnew = need ? mx : m_run;
+      const float corr = exp2f(m_run - mnew);
+      m_run = mnew;
       float ps = 0.f;
       v4i pk;
 #pragma unroll
@@ -228,68 +225,70 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
         ps += p0 + p1;
         pk[i] = (int)pack_bf16x2(p0, p1);
       }
-      l_part[hs] = l_part[hs] * corr[hs] + ps;
-      pb[hs] = (v8s)pk;
+      l_part = l_part * corr + ps;
+      *(v4i*)(pbuf + (w * 64 + lane) * 16) = pk;
+      if (g == 0) s_corr[16 * w + c] = corr;
+      const bool any = __any(need);
+      if (lane == 0) s_need[w] = any ? 1 : 0;
     }
-    return __any(need_any);
-  };
-  // O^T += V^T . P^T for one tile; V^T fragment via two transposed reads
-  auto pv = [&](int tile, const v8s (&pb)[HS]) {
-    const char* tp = smem + (tile % NBUF) * TILE_BYTES;
-    const char* vb = SEPV ? tp + KF * 1024 : tp;
+    __syncthreads();
+    // a head whose max moved: rescale its O columns (all waves hold them)
+    bool resc = false;
 #pragma unroll
-    for (int d = 0; d < DV / 16; ++d) {
-      const int off = vbase + ((d >> 1) * 4 + 2 * (d & 1)) * 256;
-      const v4s lo = lds_read_tr16(vb, off);
-      const v4s hi = lds_read_tr16(vb, off + VF * 1024);
-      const v8s av = (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int i = 0; i < NW; ++i) resc |= s_need[i] != 0;
+    if (resc) {
 #pragma unroll
-      for (int hs = 0; hs < HS; ++hs) o[d][hs] = mfma_bf16_16x16x32(av, pb[hs], o[d][hs]);
-      if (d % DSA_PV_GROUP == DSA_PV_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+      for (int hs = 0; hs < NW; ++hs) {
+        const float cr = s_corr[16 * hs + c];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[d][hs] *= cr;
+      }
     }
-  };
-  auto rescale = [&](const float (&corr)[HS]) {
+    // O^T += V^T . P^T over this wave's value columns
+    {
+      const char* vb = SEPV ? tb + KF * 1024 : tb;
+      v8s av[ND];
 #pragma unroll
-    for (int hs = 0; hs < HS; ++hs)
+      for (int d = 0; d < ND; ++d) {
+        const int D = ND * w + d;                 // value subtile index
+        const int off = vbase + ((D >> 1) * 4 + 2 * (D & 1)) * 256;
+        const v4s lo = lds_read_tr16(vb, off);
+        const v4s hi = lds_read_tr16(vb, off + VF * 1024);
+        av[d] = (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
 #pragma unroll
-      for (int d = 0; d < DV / 16; ++d) o[d][hs] *= corr[hs];
-  };
-
-  // Per tile: S^T, softmax, PV.  The gather of tile it+1 is issued before
-  // tile it's math into the other buffer, which every wave finished reading
-  // before the barrier that closed the previous step.
-  if (ntiles > 0) {
-    issue_tile(0);
+      for (int hs = 0; hs < NW; ++hs) {
+        const v8s pf = *(const v8s*)(pbuf + (hs * 64 + lane) * 16);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[d][hs] = mfma_bf16_16x16x32(av[d], pf, o[d][hs]);
+        if (hs % DSA_PV_GROUP == DSA_PV_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      if (it + 1 < ntiles) issue_tile(it + 1);
-      v4f sacc[2][HS];
-      qk(it, sacc);
-      v8s pb[HS];
-      float corr[HS];
-      if (softmax(it, sacc, pb, corr)) rescale(corr);
-      pv(it, pb);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    }
   }
 
-  // epilogue: lane (c, g) holds O^T[dv = 16d + 4g + i][head HW*w + 16hs + c]
+  // epilogue: row sums of every head, then lane (c, g) of wave w writes
+  // O^T[dv = DVW*w + 16d + 4g + i][head 16hs + c]
+  {
+    const float l = rows_sum(l_part);
+    if (g == 0) s_l[16 * w + c] = l;
+    if (a.lse && g == 0) a.lse[t * H + 16 * w + c] = n > 0 ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
 #pragma unroll
-  for (int hs = 0; hs < HS; ++hs) {
-    const float l = rows_sum(l_part[hs]);
-    const int h = HW * w + 16 * hs + c;
+  for (int hs = 0; hs < NW; ++hs) {
+    const int h = 16 * hs + c;
+    const float l = s_l[h];
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV;
+    uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV + DVW * w;
 #pragma unroll
-    for (int d = 0; d < DV / 16; ++d) {
+    for (int d = 0; d < ND; ++d) {
       v2i pk;
       pk[0] = (int)pack_bf16x2(o[d][hs][0] * inv, o[d][hs][1] * inv);
       pk[1] = (int)pack_bf16x2(o[d][hs][2] * inv, o[d][hs][3] * inv);
       *(v2i*)(op + 16 * d + 4 * g) = pk;
     }
-    if (a.lse && g == 0) a.lse[t * H + h] = n > 0 ? (m_run[hs] + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -371,9 +370,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, const int64_t
   }
 }
 
-bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv) {
+// dynamic LDS a block may take (160 KB per CU, less the kernel's static LDS)
+constexpr size_t kAttnLdsLimit = 160 * 1024 - 2048;
+
+bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int64_t k) {
   if (f32) return H >= 1 && H <= 64 && Dk >= 4 && Dk <= 128 && Dv >= 4 && Dv <= 128 && Dk % 4 == 0 && Dv % 4 == 0;
-  return (H == 16 && Dk == 128 && Dv == 128) || (H == 128 && Dk == 576 && Dv == 512);
+  if (H == 16 && Dk == 128 && Dv == 128) return true;
+  if (H == 128 && Dk == 576 && Dv == 512) {
+    // two gathered tiles + P^T + the index row must fit in LDS
+    const size_t tile = (size_t)32 * (Dk / 8 + (sep_v ? Dv / 8 : 0)) * 16;
+    return 2 * tile + 8 * 1024 + (size_t)k * 4 <= kAttnLdsLimit;
+  }
+  return false;
 }
 
 size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t k) {
@@ -385,20 +393,22 @@ size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t 
   return 0;
 }
 
-template <int DK, int DV, int HW, int NW, bool SEPV>
+template <int DK, int DV, int NW, bool SEPV>
 static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
   constexpr size_t tile = (size_t)32 * (DK / 8 + (SEPV ? DV / 8 : 0)) * 16;
-  constexpr int NBUF = 2;
-  constexpr size_t lds_max = NBUF * tile + (size_t)DSA_MAX_TOPK * 4;
-  const size_t lds = NBUF * tile + (size_t)a.k * 4;
+  constexpr size_t fixed = 2 * tile + (size_t)NW * 1024;
+  constexpr size_t lds_max = fixed + (size_t)DSA_MAX_TOPK * 4 <= kAttnLdsLimit
+                                 ? fixed + (size_t)DSA_MAX_TOPK * 4 : kAttnLdsLimit;
+  const size_t lds = fixed + (size_t)a.k * 4;
+  if (lds > lds_max) return hipErrorInvalidValue;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<DK, DV, HW, NW, SEPV, NBUF>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<DK, DV, NW, SEPV>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attn_bf16_kernel<DK, DV, HW, NW, SEPV, NBUF><<<(unsigned)a.T, NW * 64, lds, st>>>(a, seq_off);
+  attn_bf16_kernel<DK, DV, NW, SEPV><<<(unsigned)a.T, NW * 64, lds, st>>>(a, seq_off);
   return hipGetLastError();
 }
 
@@ -411,12 +421,12 @@ hipError_t launch_attn(const AttnArgs& a, bool f32, void* ws, size_t ws_bytes, h
     return hipGetLastError();
   }
   if (a.H == 16 && a.Dk == 128 && a.Dv == 128) {
-    if (a.v) return launch_bf16<128, 128, 16, 1, true>(a, a.seq_offsets, st);
-    return launch_bf16<128, 128, 16, 1, false>(a, a.seq_offsets, st);
+    if (a.v) return launch_bf16<128, 128, 1, true>(a, a.seq_offsets, st);
+    return launch_bf16<128, 128, 1, false>(a, a.seq_offsets, st);
   }
   if (a.H == 128 && a.Dk == 576 && a.Dv == 512) {
-    if (a.v) return launch_bf16<576, 512, DSA_MLA_HW, DSA_MLA_NW, true>(a, a.seq_offsets, st);
-    return launch_bf16<576, 512, DSA_MLA_HW, DSA_MLA_NW, false>(a, a.seq_offsets, st);
+    if (a.v) return launch_bf16<576, 512, 8, true>(a, a.seq_offsets, st);
+    return launch_bf16<576, 512, 8, false>(a, a.seq_offsets, st);
   }
   return hipErrorInvalidValue;
 }

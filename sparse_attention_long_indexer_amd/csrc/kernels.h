@@ -57,7 +57,7 @@ struct AttnArgs {
   void* out;            // [T][H][Dv]
   float* lse;           // [T][H] or nullptr
 };
-bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv);
+bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int64_t k);
 size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t k);
 hipError_t launch_attn(const AttnArgs& a, bool f32, void* ws, size_t ws_bytes, hipStream_t st);
 
