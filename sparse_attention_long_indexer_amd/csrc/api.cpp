@@ -91,7 +91,7 @@ dsa_status_t check_attn(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dty
 // ---- dsa_forward workspace plan -----------------------------------------
 
 struct FwdPlan {
-  size_t qf_off, qs_off, idx_off, sc_off, total;
+  size_t qf_off, qs_off, idx_off, sc_off, topk_off, topk_bytes, total;
   int64_t chunk_rows;  // prefill: rows of scores materialised at once
   bool fused;          // prefill: fused scores + select
 };
@@ -135,6 +135,9 @@ FwdPlan plan_forward(const dsa_forward_args* a, bool need_idx) {
   } else {
     p.chunk_rows = R;
     off = round_up(off + (size_t)a->total_keys * 4, kAlign);
+    p.topk_off = off;
+    p.topk_bytes = topk_workspace_bytes(R, a->max_len, a->topk);
+    off = round_up(off + p.topk_bytes, kAlign);
   }
   p.total = off;
   return p;
@@ -343,7 +346,7 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
                                      a->seq_offsets, R, a->max_len, sc, st);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
       TopkRows tr{sc, 0, nullptr, nullptr, 0, a->seq_offsets, 0};
-      e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, nullptr, st);
+      e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, p.topk_bytes ? base + p.topk_off : nullptr, st);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
       at.seq_offsets = a->seq_offsets;
       at.S = a->total_keys;

@@ -110,7 +110,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c = lane & 15;
-  const int64_t t = blockIdx.x;
+  const int64_t t = blockIdx.x / a.splits;
+  const int sp = (int)(blockIdx.x % a.splits);
   const AttnRow row = attn_row(a, seq_off, t);
   // stage the query's index row; n = leading valid entries
   if (tid == 0) s_cnt = (int)a.k;
@@ -125,7 +126,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     if (first < (int)a.k) atomicMin(&s_cnt, first);
   }
   __syncthreads();
-  const int n = s_cnt;
+  // this block's keys: [kbeg, n) of the valid entries (split in whole tiles)
+  const int nvalid = s_cnt;
+  const int per = ((nvalid + a.splits - 1) / a.splits + NK - 1) / NK * NK;
+  const int kbeg = min(nvalid, sp * per);
+  const int n = min(nvalid, kbeg + per);
   const char* kvb = (const char*)a.kv;
   const char* vvb = SEPV ? (const char*)a.v : kvb;
   const int64_t ldk = a.ld_kv * 2, ldv = (SEPV ? a.ld_v : a.ld_kv) * 2;  // bytes
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     for (int hs = 0; hs < NW; ++hs) o[d][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
   const float zs = a.scale * kLog2e;
-  const int ntiles = (n + NK - 1) / NK;
+  const int ntiles = (n - kbeg + NK - 1) / NK;
   // V^T reads: lane (sl, G) reads row 4G + sl/4 (+16h), dv 16D + 4(sl%4):
   // chunk X = 2D + (sl%4)/2, half sl%2, i.e. slot
   // ((h*VF + D/2)*4 + 2(D%2) + (sl%4)/2)*16 + 4G + sl/4.
@@ -180,13 +185,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   // LDS, then O^T for all heads over the wave's value columns.  The gather
   // of tile it+1 is issued first, into the buffer every wave finished
   // reading before the barrier that closed the previous tile.
+  const int t0 = kbeg / NK;  // first tile of this split
   if (ntiles > 0) {
-    issue_tile(0);
+    issue_tile(t0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) issue_tile(it + 1);
+  for (int it = t0; it < t0 + ntiles; ++it) {
+    if (it + 1 < t0 + ntiles) issue_tile(it + 1);
     const char* tb = smem + (it & 1) * TILE_BYTES;
     const int j0 = it * NK;
     // S^T = K . Q^T (key subtiles ks = rows 16ks + c)
@@ -269,27 +275,85 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   }
 
   // epilogue: row sums of every head, then lane (c, g) of wave w writes
-  // O^T[dv = DVW*w + 16d + 4g + i][head 16hs + c]
+  // O^T[dv = DVW*w + 16d + 4g + i][head 16hs + c]: normalised bf16 output,
+  // or with several splits the unnormalised fp32 partial plus (max, sum)
+  const bool partial = a.splits > 1;
   {
     const float l = rows_sum(l_part);
     if (g == 0) s_l[16 * w + c] = l;
-    if (a.lse && g == 0) a.lse[t * H + 16 * w + c] = n > 0 ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    if (g == 0) {
+      const int h = 16 * w + c;
+      if (partial) {
+        float* ml = a.part_ml + ((t * a.splits + sp) * H + h) * 2;
+        ml[0] = m_run;
+        ml[1] = l;
+      } else if (a.lse) {
+        a.lse[t * H + h] = n > 0 ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int hs = 0; hs < NW; ++hs) {
     const int h = 16 * hs + c;
-    const float l = s_l[h];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV + DVW * w;
+    if (partial) {
+      float* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + DVW * w;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      v2i pk;
-      pk[0] = (int)pack_bf16x2(o[d][hs][0] * inv, o[d][hs][1] * inv);
-      pk[1] = (int)pack_bf16x2(o[d][hs][2] * inv, o[d][hs][3] * inv);
-      *(v2i*)(op + 16 * d + 4 * g) = pk;
+      for (int d = 0; d < ND; ++d) *(v4f*)(op + 16 * d + 4 * g) = o[d][hs];
+    } else {
+      const float l = s_l[h];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV + DVW * w;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        v2i pk;
+        pk[0] = (int)pack_bf16x2(o[d][hs][0] * inv, o[d][hs][1] * inv);
+        pk[1] = (int)pack_bf16x2(o[d][hs][2] * inv, o[d][hs][3] * inv);
+        *(v2i*)(op + 16 * d + 4 * g) = pk;
+      }
     }
   }
+}
+
+// merge the key splits of each (query, head): weights 2^(m_s - M) with M the
+// largest split max; out = sum_s w_s O_s / sum_s w_s l_s (bf16), lse in ln.
+// Dv/4 threads per (query, head), four value columns each.
+constexpr int kMaxSplits = 8;
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int tph = (int)(a.Dv / 4);
+  const int per_blk = 256 / tph;
+  const int64_t th = (int64_t)blockIdx.x * per_blk + threadIdx.x / tph;
+  if ((int)threadIdx.x >= per_blk * tph || th >= a.T * a.H) return;
+  const int d = 4 * (threadIdx.x % tph);
+  const int64_t t = th / a.H, h = th % a.H;
+  const int S = a.splits;
+  float ms[kMaxSplits], ls[kMaxSplits];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < S) {
+      const float2 ml = *(const float2*)(a.part_ml + ((t * S + s) * a.H + h) * 2);
+      ms[s] = ml.x;
+      ls[s] = ml.y;
+      M = fmaxf(M, ml.x);
+    }
+  }
+  float L = 0.f;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < S && ls[s] > 0.f) {
+      const float wgt = exp2f(ms[s] - M);
+      L += ls[s] * wgt;
+      acc += wgt * *(const v4f*)(a.part_o + ((t * S + s) * a.H + h) * a.Dv + d);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  v2i pk;
+  pk[0] = (int)pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk[1] = (int)pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(v2i*)((uint16_t*)a.out + (t * a.H + h) * a.Dv + d) = pk;
+  if (a.lse && d == 0) a.lse[t * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---- fp32 path -----------------------------------------------------------
@@ -384,13 +448,23 @@ bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int
   return false;
 }
 
+// key splits per query: about one block per CU when there are few queries
+// (batched decode; a block fills a CU's LDS); each split keeps at least 8
+// tiles of keys
+static int attn_splits(bool f32, int64_t T, int64_t k) {
+  if (f32 || T <= 0 || T >= 256) return 1;
+  int s = (int)((256 + T - 1) / T);
+  const int maxs = (int)(k / 256);
+  if (s > maxs) s = maxs;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : s;
+}
+
 size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t k) {
-  (void)f32;
-  (void)T;
-  (void)H;
-  (void)Dv;
-  (void)k;
-  return 0;
+  const int s = attn_splits(f32, T, k);
+  if (s <= 1) return 0;
+  const size_t o = (size_t)T * s * H * Dv * 4, ml = (size_t)T * s * H * 2 * 4;
+  return (o + 255) / 256 * 256 + ml;
 }
 
 template <int DK, int DV, int NW, bool SEPV>
@@ -408,15 +482,25 @@ static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStre
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attn_bf16_kernel<DK, DV, NW, SEPV><<<(unsigned)a.T, NW * 64, lds, st>>>(a, seq_off);
+  attn_bf16_kernel<DK, DV, NW, SEPV><<<(unsigned)(a.T * a.splits), NW * 64, lds, st>>>(a, seq_off);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  const int64_t per_blk = 256 / (a.Dv / 4);
+  attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnArgs& a, bool f32, void* ws, size_t ws_bytes, hipStream_t st) {
-  (void)ws;
-  (void)ws_bytes;
-  if (a.T <= 0) return hipSuccess;
+hipError_t launch_attn(const AttnArgs& a_in, bool f32, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (a_in.T <= 0) return hipSuccess;
+  AttnArgs a = a_in;
+  a.splits = attn_splits(f32, a.T, a.k);
+  if (a.splits > 1) {
+    if (!ws || ws_bytes < attn_workspace_bytes(f32, a.T, a.H, a.Dv, a.k)) return hipErrorInvalidValue;
+    a.part_o = (float*)ws;
+    a.part_ml = (float*)((char*)ws + ((size_t)a.T * a.splits * a.H * a.Dv * 4 + 255) / 256 * 256);
+  }
   if (f32) {
+    a.splits = 1;
     attn_f32_kernel<<<(unsigned)a.T, 256, 0, st>>>(a, a.seq_offsets);
     return hipGetLastError();
   }

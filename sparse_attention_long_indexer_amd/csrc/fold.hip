@@ -13,9 +13,9 @@
 
 namespace dsa {
 
-constexpr int kFoldRows = 32;
-
-template <bool kFp8In, bool kWBf16>
+// rows per block: 32 for long prefills; small batches (decode) use 2 so the
+// launch still spreads over many CUs
+template <bool kFp8In, bool kWBf16, int kFoldRows>
 __global__ __launch_bounds__(128) void fold_kernel(const void* __restrict__ q_in,
                                                    const float* __restrict__ q_scale,
                                                    const void* __restrict__ w_in, int64_t T,
@@ -77,16 +77,25 @@ __global__ __launch_bounds__(128) void fold_kernel(const void* __restrict__ q_in
   }
 }
 
+template <int R>
+static void launch_fold_rows(const void* q_in, const float* q_scale, bool fp8_in, const void* w, bool w_bf16,
+                             int64_t T, void* q_out, float* s_out, hipStream_t st) {
+  dim3 grid((unsigned)((T + R - 1) / R));
+  if (fp8_in && w_bf16)
+    fold_kernel<true, true, R><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+  else if (fp8_in)
+    fold_kernel<true, false, R><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+  else
+    fold_kernel<false, false, R><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+}
+
 hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, const void* w,
                        bool w_bf16, int64_t T, void* q_out, float* s_out, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  dim3 grid((unsigned)((T + kFoldRows - 1) / kFoldRows));
-  if (fp8_in && w_bf16)
-    fold_kernel<true, true><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
-  else if (fp8_in)
-    fold_kernel<true, false><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+  if (T >= 8192)
+    launch_fold_rows<32>(q_in, q_scale, fp8_in, w, w_bf16, T, q_out, s_out, st);
   else
-    fold_kernel<false, false><<<grid, 128, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+    launch_fold_rows<2>(q_in, q_scale, fp8_in, w, w_bf16, T, q_out, s_out, st);
   return hipGetLastError();
 }
 

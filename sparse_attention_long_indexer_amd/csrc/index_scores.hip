@@ -114,30 +114,41 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
 // ---- decode: one query per sequence against its own cache ----------------
 //
 // Bound by the HBM read of the cached index keys (132 bytes per key with its
-// scale).  Block (x, b) covers 256 keys of sequence b; the query row is
-// replicated over the 16 A rows so every C row holds the same 16 scores.
-constexpr int kDecKeysPerBlock = 256;
+// scale).  Block (x, b) covers 512 keys of sequence b, 128 per wave; the
+// query row is replicated over the 16 A rows so every C row holds the same
+// 16 scores.  Every key and scale load of a wave is issued before the first
+// MFMA (clamped addresses, no branches), so each wave keeps 16 KB in flight.
+constexpr int kDecWaveKeys = 128;
+constexpr int kDecKeysPerBlock = 4 * kDecWaveKeys;
 
 __global__ __launch_bounds__(256) void index_scores_decode_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const int64_t* __restrict__ off, float* __restrict__ out) {
+  constexpr int J = kDecWaveKeys / 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int64_t b = blockIdx.y;
   const int64_t lo = off[b], n = off[b + 1] - lo;
-  const int64_t sw = (int64_t)blockIdx.x * kDecKeysPerBlock + w * 64;
+  const int64_t sw = (int64_t)blockIdx.x * kDecKeysPerBlock + w * kDecWaveKeys;
   if (sw >= n) return;
+  v8i bb[J];
+  float kss[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t s = sw + 16 * j + c;
+    const int64_t sb = lo + (s < n ? s : n - 1);
+    bb[j] = *(const v8i*)(k + sb * kIdxDim + 32 * g);
+    kss[j] = ks[sb];
+  }
   const v8i a = *(const v8i*)(qf + b * kIdxDim + 32 * g);
   const float qsc = qs[b];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int64_t s = sw + 16 * j + c;
-    const int64_t sb = lo + (s < n ? s : n - 1);
-    const v8i bb = *(const v8i*)(k + sb * kIdxDim + 32 * g);
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma_fp8_16x16x128(a, bb, acc);
+    acc = mfma_fp8_16x16x128(a, bb[j], acc);
     if (g == 0 && s < n) {
-      const float u = acc[0] * ks[sb] * qsc;
+      const float u = acc[0] * kss[j] * qsc;
       out[lo + s] = u > 0.f ? u : 0.f;
     }
   }

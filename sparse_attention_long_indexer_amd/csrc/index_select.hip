@@ -495,60 +495,12 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   uint32_t thr, need;
   radix_select<kSelThreads>([&](int64_t e) { return cl[e].x; }, nslots, (uint32_t)m, lo, mx, hist, wave_cnt,
                             s_sel, thr, need);
-  // keys above the m-th best go to the bitmap; ties go to a list
-  for (int e = tid; e < nslots; e += kSelThreads) {
-    const uint2 cv = cl[e];
-    const uint32_t key = cv.x;
-    const int32_t p = (int32_t)cv.y;
-    if (key < thr || p < 0 || p >= n) continue;  // also skips invalid slots (key 0)
-    if (key > thr) {
-      atomicOr(&sel[p >> 5], 1u << (p & 31));
-    } else {
-      const int q = atomicAdd(&s_ntie, 1);
-      if (q < kMaxTies) s_tie[q] = p;
-    }
-  }
-  __syncthreads();
-  const int ntie = s_ntie;
-  if (ntie > kMaxTies) {  // a pathological tie at the boundary: settle exactly elsewhere
+  // keys above the m-th best go to the bitmap, ties to a list; a
+  // pathological tie at the boundary is settled exactly elsewhere
+  if (!output_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel, nwords, s_tie, kMaxTies,
+                                           &s_ntie, wave_cnt, o)) {
     if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
-    return;
   }
-  // keep the `need` lowest-position ties
-  for (int i = tid; i < ntie; i += kSelThreads) {
-    const int32_t p = s_tie[i];
-    int rank = 0;
-    for (int j = 0; j < ntie; ++j) rank += s_tie[j] < p ? 1 : 0;
-    if (rank < (int)need) atomicOr(&sel[p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
-  // ascending output: prefix popcount over the bitmap
-  const int per = (nwords + kSelThreads - 1) / kSelThreads;
-  const int w0 = tid * per, w1 = min(nwords, w0 + per);
-  uint32_t mine = 0;
-  for (int i = w0; i < w1; ++i) mine += __popc(sel[i]);
-  {
-    uint32_t incl = mine;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) wave_cnt[w] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    for (int i = 0; i < kSelWaves; ++i) before += (i < w) ? wave_cnt[i] : 0u;
-    uint32_t pos = before + incl - mine;
-    for (int i = w0; i < w1; ++i) {
-      uint32_t wv = sel[i];
-      while (wv) {
-        const int b = __builtin_ctz(wv);
-        if (pos < (uint32_t)m) o[pos] = i * 32 + b;
-        ++pos;
-        wv &= wv - 1;
-      }
-    }
-  }
-  for (int64_t i = m + tid; i < topk; i += kSelThreads) o[i] = -1;
 }
 
 // ---- 4. exact fallback for rows the survivors cannot settle ---------------

@@ -1,5 +1,5 @@
-// Row selection shared by the standalone top-k and the fused indexer's
-// exact fallback.
+// Row selection shared by the standalone top-k, the candidate top-k for few
+// long rows and the fused indexer.
 #pragma once
 
 #include "common.h"
@@ -36,9 +36,6 @@ __device__ __forceinline__ uint32_t block_prefix(bool pred, uint32_t* wave_cnt, 
   return before + lanes_below(m);
 }
 
-// Exact top-k of one row p[0..n) by (score desc, index asc), written in
-// ascending index order to o[0..k) with -1 padding.  All kTopkThreads
-// threads of the block call it; `sh` is block-shared scratch.
 // Block-wide exact selection of the m-th largest 32-bit key among n keys
 // (key_at(i) for i < n) that are >= lo, given every key is <= hi and at
 // least m keys are >= lo.  Radix over d = key - lo with 10-bit digits, so
@@ -122,6 +119,9 @@ __device__ inline void radix_select(KeyAt key_at, int64_t n, uint32_t m, uint32_
   need = remaining;
 }
 
+// Exact top-k of one row p[0..n) by (score desc, index asc), written in
+// ascending index order to o[0..k) with -1 padding.  All kTopkThreads
+// threads of the block call it; `sh` is block-shared scratch.
 __device__ inline void select_row(const float* __restrict__ p, int64_t n, int64_t k, int32_t* __restrict__ o,
                                   TopkShared& sh) {
   const int tid = threadIdx.x;
@@ -172,6 +172,73 @@ __device__ inline void select_row(const float* __restrict__ p, int64_t n, int64_
     carry_sel += tot_sel;
   }
   for (int64_t i = m + tid; i < k; i += kTopkThreads) o[i] = -1;
+}
+
+// Ascending output from a candidate list: given thr / need from radix_select
+// over the (key, position) pairs cl[0 .. nslots) of a row of n keys, keep
+// every position whose key is above thr and the `need` lowest positions
+// whose key equals thr, and write the m kept positions in ascending order to
+// o[0 .. m), padding o[m .. topk) with -1.  Kept positions are marked in a
+// bitmap of nwords words (zeroed by the caller, as is *s_ntie); keys equal
+// to thr go through the tie list `tie` (max_ties entries).  Positions outside
+// [0, n) are skipped (invalid slots).  Returns false, with nothing written
+// to o, when the tie list overflows; the caller settles the row elsewhere.
+template <int NT>
+__device__ inline bool output_from_candidates(const uint2* cl, int nslots, uint32_t thr, uint32_t need,
+                                              int64_t n, int64_t m, int64_t topk, uint32_t* bitmap,
+                                              int nwords, int32_t* tie, int max_ties, int* s_ntie,
+                                              uint32_t* wave_cnt, int32_t* __restrict__ o) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < nslots; e += NT) {
+    const uint2 cv = cl[e];
+    const uint32_t key = cv.x;
+    const int32_t p = (int32_t)cv.y;
+    if (key < thr || p < 0 || p >= n) continue;
+    if (key > thr) {
+      atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+    } else {
+      const int q = atomicAdd(s_ntie, 1);
+      if (q < max_ties) tie[q] = p;
+    }
+  }
+  __syncthreads();
+  const int ntie = *s_ntie;
+  if (ntie > max_ties) return false;
+  for (int i = tid; i < ntie; i += NT) {
+    const int32_t p = tie[i];
+    int rank = 0;
+    for (int j = 0; j < ntie; ++j) rank += tie[j] < p ? 1 : 0;
+    if (rank < (int)need) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // prefix popcount over the bitmap: thread tid owns a run of `per` words
+  const int per = (nwords + NT - 1) / NT;
+  const int w0 = tid * per, w1 = min(nwords, w0 + per);
+  uint32_t mine = 0;
+  for (int i = w0; i < w1; ++i) mine += __popc(bitmap[i]);
+  uint32_t incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wave_cnt[w] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) before += (i < w) ? wave_cnt[i] : 0u;
+  uint32_t pos = before + incl - mine;
+  for (int i = w0; i < w1; ++i) {
+    uint32_t wv = bitmap[i];
+    while (wv) {
+      const int b = __builtin_ctz(wv);
+      if (pos < (uint32_t)m) o[pos] = i * 32 + b;
+      ++pos;
+      wv &= wv - 1;
+    }
+  }
+  for (int64_t i = m + tid; i < topk; i += NT) o[i] = -1;
+  return true;
 }
 
 }  // namespace dsa

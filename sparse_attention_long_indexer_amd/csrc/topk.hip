@@ -1,16 +1,24 @@
 // Per-row top-k selection over materialised scores (DeepSeek-V3.2 write-up,
 // section 2.3: keep the k best-scoring keys of each query).
 //
-// One 1024-thread block per row.  Scores map to order-preserving uint32 keys
-// (larger score -> larger key, -0.0 folded onto +0.0).  A most-significant-
-// digit-first radix select with four 8-bit digits finds the exact key of the
-// m-th best element and how many elements equal to it are kept; LDS
-// histograms take one atomic per element, except the key of a zero score,
-// which ReLU makes the common tie and which is counted with a wave ballot.
-// A last pass walks the row in index order with block-wide prefix counts
-// (wave ballots + per-wave totals in LDS), keeps every key above the
-// threshold and the lowest-index keys equal to it, and writes the kept
-// indices in ascending order.
+// Scores map to order-preserving uint32 keys (larger score -> larger key,
+// -0.0 folded onto +0.0).  Two strategies give the same exact result:
+//
+// Many rows: one 1024-thread block per row.  A most-significant-digit-first
+// radix select over the row's key range finds the exact key of the m-th
+// best element and how many elements equal to it are kept; a last pass
+// walks the row in index order with block-wide prefix counts, keeps every
+// key above that threshold and the lowest-index keys equal to it, and
+// writes the kept indices in ascending order.
+//
+// Few long rows (batched decode): one block per row would leave most of the
+// chip idle, so the row is cut down first.  A sampled estimate picks a
+// threshold key tau per row that about 1.75 m keys reach; a wide filter
+// pass over every row appends the keys >= tau to a per-row candidate list;
+// one block per row then selects exactly among the candidates.  When at
+// least m keys reach tau, the top m are all candidates, so the result is
+// exact; a row with too few or too many candidates (or a pathological tie)
+// is settled by the one-block-per-row select instead.
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -49,19 +57,295 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(TopkRows R, in
   select_row(rv.p, rv.n, k, idx_out + row * k, sh);
 }
 
+// ---- candidate path for few long rows --------------------------------------
+constexpr int kCandCap = 8192;          // candidates a row may stage in LDS
+constexpr int kCandWin = 64;            // sampled keys per window (one wave)
+constexpr int kCandWins = 64;           // windows per row, one per stratum
+constexpr int kCandSample = kCandWin * kCandWins;
+constexpr int kCandSpan = 4096;         // keys per filter block
+constexpr int kCandThreads = 512;
+constexpr int kCandWaves = kCandThreads / 64;
+constexpr int kCandMaxTies = 512;
+constexpr int64_t kCandMinN = 16384;    // shorter rows: one block per row is enough
+constexpr int64_t kCandMaxN = 524288;   // the bitmap of kept positions fits in LDS
+constexpr int64_t kCandMaxRows = 512;   // more rows fill the chip one block per row
+constexpr int kCandFbBlocks = 64;
+
+static bool topk_use_candidates(int64_t rows, int64_t max_n, int64_t k) {
+  return rows >= 1 && rows < kCandMaxRows && max_n >= kCandMinN && max_n <= kCandMaxN && 2 * k <= kCandCap;
+}
+
+// integer hash (the "lowbias32" mixer) for window offsets
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// tau[row]: the r-th largest of 4096 sampled keys (one 64-key window at a
+// hashed offset inside each of 64 equal strata), r chosen so that about
+// min(1.75 m, (m + cap) / 2) keys of the row reach it.  0 (below every key)
+// when the whole row fits the candidate list.  A threshold on the zero
+// score is raised past it, so ReLU's zeros do not flood the list.  Also
+// clears the row's candidate count and (block 0) the fallback queue.
+__global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRows R, int64_t k,
+                                                                         uint32_t* __restrict__ tau,
+                                                                         int32_t* __restrict__ cnt,
+                                                                         int32_t* __restrict__ fb) {
+  __shared__ uint32_t skey[kCandSample];
+  __shared__ uint32_t hist[1024];
+  __shared__ uint32_t scan[kCandWaves];
+  __shared__ uint32_t s_out[2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t row = blockIdx.x;
+  if (tid == 0) {
+    cnt[row] = 0;
+    if (row == 0) fb[0] = 0;
+  }
+  const RowView rv = topk_row_view(R, row);
+  const int64_t n = rv.n, m = n < k ? n : k;
+  if (n <= kCandCap) {
+    if (tid == 0) tau[row] = 0u;
+    return;
+  }
+  const double target = fmin(1.75 * (double)m, 0.5 * (double)(m + kCandCap));
+  int64_t r = (int64_t)ceil(target * kCandSample / (double)n);
+  r = r < 1 ? 1 : (r > kCandSample ? kCandSample : r);
+  constexpr int WPW = kCandWins / kCandWaves;  // windows per wave
+  float v[WPW];
+#pragma unroll
+  for (int q = 0; q < WPW; ++q) {
+    const int wi = w + q * kCandWaves;
+    const int64_t s0 = n * wi / kCandWins, s1 = n * (wi + 1) / kCandWins;
+    const uint64_t slots = (uint64_t)(s1 - s0 - kCandWin + 1);  // n > cap, so >= 65
+    const int64_t start = s0 + (int64_t)(mix32((uint32_t)(row * kCandWins + wi) ^ 0x9e3779b9u) % slots);
+    v[q] = rv.p[start + lane];
+  }
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int q = 0; q < WPW; ++q) {
+    const uint32_t key = score_key(v[q]);
+    skey[(w + q * kCandWaves) * kCandWin + lane] = key;
+    mn = min(mn, key);
+    mx = max(mx, key);
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    hist[w] = mn;
+    hist[kCandWaves + w] = mx;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < kCandWaves; ++i) {
+    mn = min(mn, hist[i]);
+    mx = max(mx, hist[kCandWaves + i]);
+  }
+  __syncthreads();
+  uint32_t thr, need;
+  radix_select<kCandThreads>([&](int64_t i) { return skey[i]; }, kCandSample, (uint32_t)r, mn, mx, hist, scan,
+                             s_out, thr, need);
+  if (tid == 0) tau[row] = thr == kZeroKey ? kZeroKey + 1 : thr;
+}
+
+// Append (key, position) of every key >= tau[row] in this block's span of
+// the row to cand[row]; cnt[row] counts them all, slots past the cap are
+// not written.  One atomic per block.
+__global__ __launch_bounds__(256) void topk_cand_filter_kernel(TopkRows R, const uint32_t* __restrict__ tau,
+                                                              uint2* __restrict__ cand, int32_t* __restrict__ cnt) {
+  constexpr int PER = kCandSpan / 256;
+  const int64_t row = blockIdx.y;
+  const RowView rv = topk_row_view(R, row);
+  const int64_t base = (int64_t)blockIdx.x * kCandSpan;
+  if (base >= rv.n) return;
+  const uint32_t tk = tau[row];
+  const int tid = threadIdx.x, lane = tid & 63;
+  // every load issued before the first compare (clamped, no branches)
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t i = base + j * 256 + tid;
+    v[j] = rv.p[i < rv.n ? i : rv.n - 1];
+  }
+  uint32_t keys[PER];
+  uint32_t mask = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t i = base + j * 256 + tid;
+    keys[j] = score_key(v[j]);
+    mask |= (i < rv.n && keys[j] >= tk) ? (1u << j) : 0u;
+  }
+  const uint32_t mine = (uint32_t)__popc(mask);
+  uint32_t incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  // one atomic per block: wave totals in LDS, thread 0 reserves the run
+  __shared__ uint32_t s_wt[4], s_base;
+  const int w = tid >> 6;
+  if (lane == 63) s_wt[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t tot = s_wt[0] + s_wt[1] + s_wt[2] + s_wt[3];
+    s_base = tot ? (uint32_t)atomicAdd(&cnt[row], (int32_t)tot) : 0u;
+  }
+  __syncthreads();
+  uint32_t pos = s_base + incl - mine;
+  for (int i = 0; i < w; ++i) pos += s_wt[i];
+  uint2* cr = cand + row * kCandCap;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if ((mask >> j) & 1u) {
+      if (pos < (uint32_t)kCandCap) cr[pos] = make_uint2(keys[j], (uint32_t)(base + j * 256 + tid));
+      ++pos;
+    }
+  }
+}
+
+// Exact top m of a row from its candidates (radix select in LDS, ascending
+// output through a bitmap of kept positions); rows the candidates cannot
+// settle go to the fallback queue fb.
+__global__ __launch_bounds__(kCandThreads) void topk_cand_select_kernel(TopkRows R, int64_t k,
+                                                                       const uint32_t* __restrict__ tau,
+                                                                       const uint2* __restrict__ cand,
+                                                                       const int32_t* __restrict__ cnt,
+                                                                       int32_t* __restrict__ idx_out,
+                                                                       int32_t* __restrict__ count_out,
+                                                                       int32_t* __restrict__ fb) {
+  extern __shared__ __align__(16) uint32_t sm[];
+  uint2* cl = (uint2*)sm;                  // [kCandCap] (key, position)
+  uint32_t* bitmap = sm + 2 * kCandCap;    // [nwords]
+  __shared__ uint32_t hist[1024];
+  __shared__ uint32_t wave_cnt[kCandWaves];
+  __shared__ uint32_t s_sel[2];
+  __shared__ int32_t s_tie[kCandMaxTies];
+  __shared__ int s_ntie;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const RowView rv = topk_row_view(R, row);
+  const int64_t n = rv.n, m = n < k ? n : k;
+  int32_t* o = idx_out + row * k;
+  if (count_out && tid == 0) count_out[row] = (int32_t)m;
+  if (n <= k) {
+    for (int64_t i = tid; i < k; i += kCandThreads) o[i] = i < n ? (int32_t)i : -1;
+    return;
+  }
+  const uint32_t tk = tau[row];
+  const int c = cnt[row];
+  if (c > kCandCap || (tk != 0u && c < m)) {
+    if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)row;
+    return;
+  }
+  const int nwords = (int)((n + 31) >> 5);
+  for (int i = tid; i < nwords; i += kCandThreads) bitmap[i] = 0u;
+  if (tid == 0) s_ntie = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  const uint2* cr = cand + row * kCandCap;
+  for (int e = tid; e < c; e += kCandThreads) {
+    const uint2 v = cr[e];
+    cl[e] = v;
+    mn = min(mn, v.x);
+    mx = max(mx, v.x);
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    hist[w] = mn;
+    hist[kCandWaves + w] = mx;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < kCandWaves; ++i) {
+    mn = min(mn, hist[i]);
+    mx = max(mx, hist[kCandWaves + i]);
+  }
+  __syncthreads();
+  uint32_t thr, need;
+  radix_select<kCandThreads>([&](int64_t e) { return cl[e].x; }, c, (uint32_t)m, tk != 0u ? tk : mn, mx, hist,
+                             wave_cnt, s_sel, thr, need);
+  if (!output_from_candidates<kCandThreads>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie, kCandMaxTies,
+                                            &s_ntie, wave_cnt, o)) {
+    if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)row;
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_cand_fallback_kernel(TopkRows R, int64_t k,
+                                                                         const int32_t* __restrict__ fb,
+                                                                         int32_t* __restrict__ idx_out) {
+  __shared__ TopkShared sh;
+  const int nfb = fb[0];
+  for (int f = blockIdx.x; f < nfb; f += gridDim.x) {
+    const int64_t row = fb[1 + f];
+    const RowView rv = topk_row_view(R, row);
+    select_row(rv.p, rv.n, k, idx_out + row * k, sh);
+    __syncthreads();
+  }
+}
+
+struct CandWs {
+  uint32_t* tau;
+  int32_t* cnt;
+  int32_t* fb;
+  uint2* cand;
+};
+
+static size_t cand_layout(int64_t rows, char* base, CandWs* out) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return base + at;
+  };
+  char* tau = take((size_t)rows * 4);
+  char* cnt = take((size_t)rows * 4);
+  char* fb = take((size_t)(rows + 1) * 4);
+  char* cand = take((size_t)rows * kCandCap * 8);
+  if (out) *out = CandWs{(uint32_t*)tau, (int32_t*)cnt, (int32_t*)fb, (uint2*)cand};
+  return off;
+}
+
 size_t topk_workspace_bytes(int64_t rows, int64_t max_n, int64_t k) {
-  (void)rows;
-  (void)max_n;
-  (void)k;
-  return 0;
+  if (!topk_use_candidates(rows, max_n, k)) return 0;
+  return cand_layout(rows, nullptr, nullptr);
 }
 
 hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k, int32_t* idx_out,
                        int32_t* count_out, void* ws, hipStream_t st) {
-  (void)max_n;
-  (void)ws;
   if (rows <= 0) return hipSuccess;
-  topk_radix_kernel<<<(unsigned)rows, kTopkThreads, 0, st>>>(r, k, idx_out, count_out);
+  if (!ws || !topk_use_candidates(rows, max_n, k)) {
+    topk_radix_kernel<<<(unsigned)rows, kTopkThreads, 0, st>>>(r, k, idx_out, count_out);
+    return hipGetLastError();
+  }
+  CandWs c;
+  cand_layout(rows, (char*)ws, &c);
+  topk_cand_estimate_kernel<<<(unsigned)rows, kCandThreads, 0, st>>>(r, k, c.tau, c.cnt, c.fb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 fgrid((unsigned)((max_n + kCandSpan - 1) / kCandSpan), (unsigned)rows);
+  topk_cand_filter_kernel<<<fgrid, 256, 0, st>>>(r, c.tau, c.cand, c.cnt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  constexpr size_t lds_max = (size_t)kCandCap * 8 + (size_t)(kCandMaxN / 32) * 4;
+  static bool attr = false;
+  if (!attr) {
+    e = hipFuncSetAttribute((const void*)topk_cand_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds_max);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const size_t lds = (size_t)kCandCap * 8 + (size_t)((max_n + 31) / 32) * 4;
+  topk_cand_select_kernel<<<(unsigned)rows, kCandThreads, lds, st>>>(r, k, c.tau, c.cand, c.cnt, idx_out,
+                                                                     count_out, c.fb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned fbb = (unsigned)(rows < kCandFbBlocks ? rows : kCandFbBlocks);
+  topk_cand_fallback_kernel<<<fbb, kTopkThreads, 0, st>>>(r, k, c.fb, idx_out);
   return hipGetLastError();
 }
 

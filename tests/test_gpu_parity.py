@@ -112,8 +112,13 @@ def test_index_scores_q_pos(dev):
 
 # ------------------------------------------------------------------ top-k ---
 
+# few long rows (T < 512, S >= 16384) take the candidate path: sampled
+# threshold, filter, select among candidates, one-block fallback; levels=1
+# leaves fewer positive scores than k, so every long row falls back
 @pytest.mark.parametrize("T,S,k,levels", [(64, 100, 1, 64), (64, 5000, 64, 8), (48, 8192, 2048, 64),
-                                           (40, 4000, 4096, 16), (8, 131072, 2048, 64), (30, 3000, 2048, 2)])
+                                           (40, 4000, 4096, 16), (8, 131072, 2048, 64), (30, 3000, 2048, 2),
+                                           (16, 40000, 1000, 4096), (6, 50000, 2048, 1),
+                                           (4, 300000, 4096, 64), (3, 20000, 2048, 2)])
 def test_topk_bit_exact(dev, T, S, k, levels):
     say("topk", T, S, k, levels)
     pos = torch.tensor(np.random.default_rng(T + S).integers(0, S, T), dtype=torch.int64)
