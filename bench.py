@@ -66,9 +66,10 @@ def load_traffic(kernel, sha):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(spec, x, rows=48, seed=0):
-    """Time the fp64 oracle on `rows` query rows drawn uniformly from the
-    workload; the per-row mean estimates the whole prefill's CPU time."""
+def cpu_baseline(spec, x, budget_s=15.0, max_rows=4096, seed=0):
+    """Time the fp64 oracle on query rows drawn uniformly from the workload
+    until about `budget_s` seconds of row work have run; the per-row mean
+    (plus the one-off setup) estimates the whole prefill's CPU time."""
     import numpy as np
     import torch
 
@@ -91,22 +92,56 @@ def cpu_baseline(spec, x, rows=48, seed=0):
     except Exception:  # pragma: no cover
         threads = 1
     rng = np.random.default_rng(seed)
-    sample = rng.integers(0, spec.L, rows)
+    sample = rng.integers(0, spec.L, max_rows)
     t0 = time.perf_counter()
     orc = od.PrefillOracle(np_(x["q_idx"]), np_(x["q_scale"]), np_(x["k_idx"]), np_(x["k_scale"]), np_(x["w"]),
                            Rows(x["q"]), np_(x["kv"]), None if x["v"] is None else np_(x["v"]), spec.topk,
                            spec.scale, spec.Dv)
     t_setup = time.perf_counter() - t0
     t1 = time.perf_counter()
+    rows = 0
     for t in sample:
         orc.row(int(t))
+        rows += 1
+        if time.perf_counter() - t1 >= budget_s:
+            break
     t_rows = time.perf_counter() - t1
     per_row = t_rows / rows
     total = t_setup + per_row * spec.L
-    return {"value": spec.L / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(spec.L / total, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} query rows drawn uniformly from the {spec.L}-token prefill "
-                      f"(setup {t_setup:.1f} s + {t_rows:.1f} s for the rows, extrapolated by the row mean)",
+                      f"(oracle setup {t_setup:.1f} s + {t_rows:.1f} s for the rows; the whole prefill "
+                      f"extrapolated as setup + L x row mean)",
             "seconds": round(t_setup + t_rows, 2)}
+
+
+def profile_attention(spec, x, reps):
+    """Launch sequence for the rocprofv3 counter runs: one known-size copy
+    (2 GiB read + 2 GiB written, the scale for FETCH_SIZE / WRITE_SIZE) and
+    `reps` sparse-attention launches of the prefill workload."""
+    import torch
+
+    from sparse_attention_long_indexer_amd import binding as B
+
+    dev = x["q"].device
+    L, k = spec.L, spec.topk
+    out = torch.empty((L, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
+    idx = torch.empty((L, k), dtype=torch.int32, device=dev)
+    fa = B.forward_args(x, k, spec.scale, spec.Dv)
+    ws = torch.empty(max(B.dsa_forward_workspace_size(fa), 256), dtype=torch.uint8, device=dev)
+    B.dsa_forward(fa, out, idx_out=idx, ws=ws)
+    del ws
+    n = 1 << 31
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for _ in range(reps):
+        B.dsa_sparse_attn(x["q"], x["kv"], idx, spec.scale, v=x["v"], Dv=spec.Dv, out=out)
+    torch.cuda.synchronize()
+    log(f"profiled: 1 copy of {n} bytes, {reps} attention launches")
 
 
 def main():
@@ -117,7 +152,9 @@ def main():
     ap.add_argument("--workload", default="prefill_L131072_mla")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="row-time budget of the CPU baseline")
+    ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
+                    help="only run the counter-profile sequence (a 2 GiB copy, then N attention launches)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -134,6 +171,9 @@ def main():
     spec = gen.WORKLOADS[args.workload]
     log("workload", spec.name, "generating inputs")
     x = gen.make_prefill(spec, seed=0, device=dev)
+    if args.profile_attn:
+        profile_attention(spec, x, args.profile_attn)
+        return
     L, k = spec.L, spec.topk
     out = torch.empty((L, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
     idx = torch.empty((L, k), dtype=torch.int32, device=dev)
@@ -171,7 +211,7 @@ def main():
     attn_ms = ev0.elapsed_time(ev1) / reps
     flops, pairs = attn_flops(L, k, spec.H, spec.Dk, spec.Dv)
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    sha = kernel_source_sha(["attn.hip", "common.h"])
+    sha = kernel_source_sha(["attn.hip", "common.h", "kernels.h"])
     traffic = load_traffic("attn_bf16_kernel<576,512,8>", sha)
     roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<576,512,8>", "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -230,7 +270,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(spec, x, rows=args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(spec, x, budget_s=args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
