@@ -156,6 +156,8 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t S, con
  * Supported (dtype, H, Dk, Dv): (F32, any H <= 64, Dk, Dv <= 128 and
  * multiples of 4), (BF16, 16, 128, 128), (BF16, 128, 576, 512); the last
  * with a separate V pointer takes k <= 3584 (its gathered tiles fill LDS).
+ * BF16 also needs S * max(ld_kv, ld_v) * 2 <= 4 GiB (rows are addressed by
+ * 32-bit byte offsets); otherwise DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_sparse_attn_workspace_size(int64_t T, int64_t H, int64_t Dv, int64_t k, dsa_dtype_t dtype);
 dsa_status_t dsa_sparse_attn(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dtype_t dtype,
@@ -175,7 +177,8 @@ dsa_status_t dsa_sparse_attn(const void* q, int64_t T, int64_t H, int64_t Dk, ds
  *   query sits at position n_b - 1 and attends over keys [0, n_b) of its
  *   own cache.  q_idx/q_scale [B][128], q [B][H][Dk]; out [B][H][Dv];
  *   idx_out [B][k] holds indices local to each sequence's cache.
- *   max_len is an upper bound on every n_b (host value, used to size work).
+ *   max_len is an upper bound on every n_b (host value, used to size work;
+ *   BF16 attention needs max_len * ld * 2 <= 4 GiB, as for dsa_sparse_attn).
  * idx_out may be NULL (the indices then live only in the workspace).
  * Workspace: dsa_forward_workspace_size(args) bytes.
  */

@@ -71,9 +71,11 @@ dsa_status_t check_scores(const void* qf, const float* qs, const void* k, const 
   return DSA_OK;
 }
 
+// rows: the most cache rows one query may address (the bf16 kernels gather
+// through 32-bit byte offsets from the query's first row)
 dsa_status_t check_attn(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dtype_t dt,
                         const void* kv, int64_t ld_kv, const void* v, int64_t ld_v, int64_t Dv,
-                        const int32_t* idx, int64_t k, const void* out) {
+                        const int32_t* idx, int64_t k, const void* out, int64_t rows) {
   if (dt != DSA_BF16 && dt != DSA_F32) return DSA_ERR_DTYPE;
   if (T < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
   if (ld_kv < Dk || (v ? ld_v < Dv : ld_kv < Dv)) return DSA_ERR_SHAPE;
@@ -84,6 +86,8 @@ dsa_status_t check_attn(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dty
     if (!aligned(q, 16) || !aligned(kv, 16) || (v && !aligned(v, 16)) || !aligned(out, 8))
       return DSA_ERR_SHAPE;
     if (ld_kv % 8 != 0 || (v && ld_v % 8 != 0)) return DSA_ERR_SHAPE;
+    const int64_t ld = v && ld_v > ld_kv ? ld_v : ld_kv;
+    if (rows > (int64_t(1) << 32) / (ld * 2)) return DSA_ERR_UNSUPPORTED;
   }
   return DSA_OK;
 }
@@ -162,8 +166,8 @@ dsa_status_t check_forward(const dsa_forward_args* a) {
     }
   }
   DSA_TRY(check_attn(a->q, a->T, a->H, a->Dk, a->attn_dtype, a->kv, a->ld_kv, a->v, a->ld_v, a->Dv,
-                     (const int32_t*)a->q /*non-null placeholder*/, a->topk, a->q));
-  (void)S;
+                     (const int32_t*)a->q /*non-null placeholder*/, a->topk, a->q,
+                     a->mode == DSA_MODE_PREFILL ? S : a->max_len));
   return DSA_OK;
 }
 
@@ -248,8 +252,8 @@ dsa_status_t dsa_sparse_attn(const void* q, int64_t T, int64_t H, int64_t Dk, ds
                              int64_t S, const int32_t* idx, int64_t k, float scale, void* out,
                              float* lse_out, void* ws, size_t ws_bytes, void* stream) {
   try {
-    DSA_TRY(check_attn(q, T, H, Dk, dtype, kv, ld_kv, v, ld_v, Dv, idx, k, out));
     if (S < 1) return DSA_ERR_SHAPE;
+    DSA_TRY(check_attn(q, T, H, Dk, dtype, kv, ld_kv, v, ld_v, Dv, idx, k, out, S));
     if (T == 0) return DSA_OK;
     const size_t need = attn_workspace_bytes(dtype == DSA_F32, T, H, Dv, k);
     if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;

@@ -3,18 +3,23 @@
 // selected keys, all query heads sharing one key/value head as in MLA's MQA
 // mode).
 //
-// bf16 path: one block per query, 16 heads per wave.  Per tile of 32
-// selected keys the block gathers the K rows (row-major) and the V rows
-// (transposed, V^T[dv][key]) into LDS, then each wave computes
-//   S^T = K . Q^T   with v_mfma_f32_16x16x32_bf16 (A = K tile from LDS,
-//                   B = the wave's Q^T held in registers for the whole loop),
-//   an online softmax per head in the log2 domain, and
-//   O^T += V^T . P^T (A = V^T from LDS, B = P^T straight from the S^T
-//                   accumulators: the C layout of S^T gives lane (head c,
-//                   group g) the keys {4g..4g+3, 16+4g..16+4g+3}, and the
-//                   V^T operand is read with the same key order).
-// Keeping heads in the N dimension puts one head per lane column, so the
-// softmax rescale of O is a per-lane scalar.
+// bf16 path: one block per query (or per key split of one), 16 heads per
+// wave.  Per tile of 32 selected keys the block gathers the rows into LDS
+// with direct-to-LDS copies (double buffered: the gather of tile i+1 runs
+// during tile i), then
+//   S^T = K . Q^T   with v_mfma_f32_16x16x32_bf16 (A = K fragments from LDS,
+//                   B = Q^T held in registers for the whole loop); for the
+//                   MLA shape, waves w and w^1 split the 576 key dims and
+//                   swap partial sums, so each K fragment read feeds two
+//                   MFMAs,
+//   an online softmax per head in the log2 domain, P^T to LDS, and
+//   O^T += V^T . P^T per wave for all heads over its own slice of the value
+//                   columns (A = V^T via transposed LDS reads, B = P^T).
+// Heads sit in the N dimension, one head per lane column, so the softmax
+// rescale of O is a per-lane scalar.  Barriers inside the loop order LDS
+// only; the gather is awaited explicitly at the end of each tile.  With few
+// queries (batched decode) the selected keys are split over blocks and an
+// LSE combine kernel merges the parts.
 //
 // fp32 path: a plain VALU kernel for the small fp32 configuration.
 #include "common.h"
@@ -65,10 +70,12 @@ __device__ __forceinline__ int valid_count(const int32_t* ip, int64_t k, int* s_
 // LDS tile of NK = 32 gathered rows, stored fragment-major: the rows form
 // two 16-row key subtiles, each row C chunks of 16 bytes; fragment
 // (ks, q) holds chunks 4q .. 4q+3 of rows 16ks .. 16ks+15 as 64 slots
-// (chunk-column major, slot = 16 * (X % 4) + row % 16).  One 16x16x32 MFMA
-// operand is then one lane-linear 1 KB read, and a transposed V read (4 rows
-// x 2 adjacent chunks per 16 lanes) covers two contiguous 256-byte runs.
-// Each gathered fragment is one 64-lane direct-to-LDS copy.
+// (chunk-column major, slot = 16 * (X % 4) + (row % 16 ^ 8 * (X % 2))).  One
+// 16x16x32 MFMA operand is then one 1 KB read whose 16-lane quarters each
+// cover 256 contiguous bytes, and a transposed V read (4 rows x 2 adjacent
+// chunks per 16 lanes) touches two 64-byte runs that the row swizzle puts on
+// different LDS banks.  Each gathered fragment is one 64-lane direct-to-LDS
+// copy.
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -80,6 +87,41 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 __device__ __forceinline__ v4s lds_read_tr16(const char* lds_base, int byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)((lds_char*)lds_base + byte_off));
 }
+
+// Eight transposed reads: value subtiles d = 0..3 (byte offsets 512 d from
+// `lds_ptr`) of key subtile 0 and of key subtile 1 (HI bytes further), into
+// av[d] = (key rows 0-15 | key rows 16-31).  One asm block that ends with
+// its own lgkmcnt wait: through the builtin, each read would also wait for
+// the direct-to-LDS gather of the next tile still in flight into the other
+// buffer, because the compiler cannot tell the two LDS regions apart.
+template <int HI>
+__device__ __forceinline__ void lds_read_vt4(const char* lds_ptr, v8s* av) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(const lds_char*)lds_ptr;
+  v2i r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:512\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:1536\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%9\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3), "=v"(r4), "=v"(r5), "=v"(r6), "=v"(r7)
+      : "v"(addr), "i"(HI), "i"(HI + 512), "i"(HI + 1024), "i"(HI + 1536)
+      : "memory");
+  const v2i lo[4] = {r0, r1, r2, r3}, hi[4] = {r4, r5, r6, r7};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const v4s l = __builtin_bit_cast(v4s, lo[d]), h = __builtin_bit_cast(v4s, hi[d]);
+    av[d] = (v8s){l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+  }
+}
+
+// split QK over the key dims between wave pairs (shared-latent shapes with
+// an even number of waves)
+constexpr bool attn_ksplit(int DK, int NW, bool SEPV) { return !SEPV && NW % 2 == 0 && (DK / 32) % 2 == 0; }
 
 template <int DK, int DV, int NW, bool SEPV>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const int64_t* seq_off) {
@@ -99,10 +141,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   constexpr int NFRAG = KF + 2 * (VC / 4);      // fragments per tile
   constexpr int LOADS = (NFRAG + NW - 1) / NW;  // fragment copies per wave per tile
   constexpr int VF = VCH / 4;
-  // dynamic LDS: [2][TILE_BYTES] tiles | [NW] P^T fragments (1 KB) | index row
+  // QK split over the key dimension: waves w and w^1 both compute S^T for
+  // heads 16w .. 16w+15 and 16(w^1) .. 16(w^1)+15, wave w over half w%2 of
+  // the Dk dims, so each K fragment read from LDS feeds two MFMAs; the pair
+  // then swaps partial sums through LDS and wave w keeps heads 16w .. 16w+15
+  // for the softmax
+  constexpr bool KSPLIT = attn_ksplit(DK, NW, SEPV);
+  constexpr int KKW = KSPLIT ? DK / 64 : DK / 32;  // k-steps of 32 dims per wave
+  constexpr int HSW = KSPLIT ? 2 : 1;              // 16-head subtiles per wave in QK
+  // dynamic LDS: [2][TILE_BYTES] tiles | [NW] P^T fragments (1 KB) |
+  // KSPLIT: [NW][2] partial S^T fragments (1 KB) | index row
   extern __shared__ __align__(16) char smem[];
   char* pbuf = smem + 2 * TILE_BYTES;
-  int32_t* sidx = (int32_t*)(pbuf + NW * 1024);
+  char* xbuf = pbuf + NW * 1024;
+  int32_t* sidx = (int32_t*)(xbuf + (KSPLIT ? NW * 2048 : 0));
   __shared__ float s_corr[H], s_l[H];
   __shared__ int s_need[NW];
   __shared__ int s_cnt;
@@ -131,16 +183,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   const int per = ((nvalid + a.splits - 1) / a.splits + NK - 1) / NK * NK;
   const int kbeg = min(nvalid, sp * per);
   const int n = min(nvalid, kbeg + per);
-  const char* kvb = (const char*)a.kv;
-  const char* vvb = SEPV ? (const char*)a.v : kvb;
-  const int64_t ldk = a.ld_kv * 2, ldv = (SEPV ? a.ld_v : a.ld_kv) * 2;  // bytes
+  // this query's cache rows start at a wave-uniform base; a row's bytes sit
+  // at a 32-bit offset from it (the launcher checks rows * ld * 2 < 4 GiB)
+  const uint32_t ldk = (uint32_t)(a.ld_kv * 2), ldv = (uint32_t)((SEPV ? a.ld_v : a.ld_kv) * 2);  // bytes
+  const char* kvq = (const char*)a.kv + row.base * (int64_t)ldk;
+  const char* vvq = SEPV ? (const char*)a.v + row.base * (int64_t)ldv : kvq;
 
   // gather: copy i of wave w fills fragment f = i*NW + w of the tile; lane
-  // l brings chunk 4q + l/16 of row 16ks + l%16 (a wave past the last
-  // fragment skips the copy, wave-uniform)
+  // l brings chunk 4q + l/16 of row 16ks + (l%16 ^ 8((l/16)%2)), so per tile
+  // a lane needs the offsets of two rows (ks = 0, 1); the chunk offset 64q
+  // is wave-uniform (a wave past the last fragment skips the copy)
+  const int rl = (lane & 15) ^ ((lane & 16) >> 1);
+  const uint32_t lofs = 16u * (uint32_t)(lane >> 4);
   auto issue_tile = [&](int tile) {
     const int j0 = tile * NK;
     char* dst = smem + (tile & 1) * TILE_BYTES;
+    const int ja = j0 + rl, jb = j0 + 16 + rl;
+    const uint32_t sa = (uint32_t)sidx[ja < n ? ja : j0], sb = (uint32_t)sidx[jb < n ? jb : j0];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + w;
@@ -149,23 +208,25 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       const int fr = isv ? f - KF : f;
       const int FQ = isv ? (VC > 0 ? VC / 4 : 1) : KC / 4;
       const int ks = fr / FQ, q = fr - ks * FQ;
-      const int r = 16 * ks + (lane & 15);
-      const int off = (4 * q + (lane >> 4)) * 16;
-      const int j = j0 + r;
-      const int64_t kr = row.base + sidx[j < n ? j : j0];
-      const char* src = isv ? vvb + kr * ldv + off : kvb + kr * ldk + off;
+      const char* src = isv ? vvq + 64 * q + ((ks ? sb : sa) * ldv + lofs)
+                            : kvq + 64 * q + ((ks ? sb : sa) * ldk + lofs);
       __builtin_amdgcn_global_load_lds((const void*)src,
                                        (__attribute__((address_space(3))) void*)((lds_char*)dst + f * 1024), 16, 0,
                                        0);
     }
   };
 
-  // Q^T fragments of head 16w + c, dims 32kk + 8g .. +8
-  v8s qf[DK / 32];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + ((t * H) + 16 * w + c) * (int64_t)DK + 8 * g;
+  // Q^T fragments, dims 32(kk0 + kk) + 8g .. +8, of head 16w + c (subtile
+  // HSW-1, kept) and, when split, of the partner's head 16(w^1) + c
+  // (subtile 0, handed over)
+  const int kk0 = KSPLIT ? (w & 1) * KKW : 0;
+  v8s qf[HSW][KKW];
 #pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) qf[kk] = *(const v8s*)(qp + 32 * kk);
+  for (int hs = 0; hs < HSW; ++hs) {
+    const int hq = (hs == HSW - 1 ? 16 * w : 16 * (w ^ 1)) + c;
+    const uint16_t* qp = (const uint16_t*)a.q + ((t * H) + hq) * (int64_t)DK + 8 * g + 32 * kk0;
+#pragma unroll
+    for (int kk = 0; kk < KKW; ++kk) qf[hs][kk] = *(const v8s*)(qp + 32 * kk);
   }
   // O^T accumulators: value subtile d of this wave's columns x head subtile hs
   v4f o[ND][NW];
@@ -178,8 +239,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   const int ntiles = (n - kbeg + NK - 1) / NK;
   // V^T reads: lane (sl, G) reads row 4G + sl/4 (+16h), dv 16D + 4(sl%4):
   // chunk X = 2D + (sl%4)/2, half sl%2, i.e. slot
-  // ((h*VF + D/2)*4 + 2(D%2) + (sl%4)/2)*16 + 4G + sl/4.
-  const int vbase = ((((lane & 3) >> 1) * 16) + 4 * (lane >> 4) + ((lane & 15) >> 2)) * 16 + (lane & 1) * 8;
+  // ((h*VF + D/2)*4 + 2(D%2) + (sl%4)/2)*16 + ((4G + sl/4) ^ 8((sl%4)/2)).
+  const int vbase =
+      ((((lane & 3) >> 1) * 16) + ((4 * (lane >> 4) + ((lane & 15) >> 2)) ^ (((lane >> 1) & 1) << 3))) * 16 +
+      (lane & 1) * 8;
+  const int kslot = lane ^ ((lane & 16) >> 1);  // lane's MFMA operand slot in a fragment
 
   // Per tile: S^T and softmax for the wave's 16 heads, P^T published to
   // LDS, then O^T for all heads over the wave's value columns.  The gather
@@ -196,15 +260,34 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     const char* tb = smem + (it & 1) * TILE_BYTES;
     const int j0 = it * NK;
     // S^T = K . Q^T (key subtiles ks = rows 16ks + c)
-    v4f sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    v4f sacc[2][HSW];
 #pragma unroll
-    for (int kk = 0; kk < DK / 32; ++kk) {
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int hs = 0; hs < HSW; ++hs) sacc[ks][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KKW; ++kk) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const v8s kf = *(const v8s*)(tb + ((ks * (KC / 4) + kk) * 64 + lane) * 16);
-        sacc[ks] = mfma_bf16_16x16x32(kf, qf[kk], sacc[ks]);
+        const v8s kf = *(const v8s*)(tb + ((ks * (KC / 4) + kk0 + kk) * 64 + kslot) * 16);
+#pragma unroll
+        for (int hs = 0; hs < HSW; ++hs) sacc[ks][hs] = mfma_bf16_16x16x32(kf, qf[hs][kk], sacc[ks][hs]);
       }
       if (kk % DSA_QK_GROUP == DSA_QK_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    v4f sc[2];
+    if constexpr (KSPLIT) {
+      // hand the partner wave its heads' partial sums, add the partner's
+      // half to ours
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) *(v4f*)(xbuf + ((w * 2 + ks) * 64 + lane) * 16) = sacc[ks][0];
+      lds_barrier();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        sc[ks] = sacc[ks][HSW - 1] + *(const v4f*)(xbuf + (((w ^ 1) * 2 + ks) * 64 + lane) * 16);
+    } else {
+      sc[0] = sacc[0][0];
+      sc[1] = sacc[1][0];
     }
     // online softmax (log2 domain); the running max only moves when a tile
     // raises it by more than 2^8, so O is rescaled rarely
@@ -212,8 +295,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       float zt[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        zt[i] = (j0 + 4 * g + i < n) ? sacc[0][i] * zs : -INFINITY;
-        zt[4 + i] = (j0 + 16 + 4 * g + i < n) ? sacc[1][i] * zs : -INFINITY;
+        zt[i] = (j0 + 4 * g + i < n) ? sc[0][i] * zs : -INFINITY;
+        zt[4 + i] = (j0 + 16 + 4 * g + i < n) ? sc[1][i] * zs : -INFINITY;
       }
       float mx = zt[0];
 #pragma unroll
@@ -237,7 +320,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       const bool any = __any(need);
       if (lane == 0) s_need[w] = any ? 1 : 0;
     }
-    __syncthreads();
+    lds_barrier();  // the gather of tile it+1 may still be in flight
     // a head whose max moved: rescale its O columns (all waves hold them)
     bool resc = false;
 #pragma unroll
@@ -254,13 +337,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     {
       const char* vb = SEPV ? tb + KF * 1024 : tb;
       v8s av[ND];
+      if constexpr (ND == 4) {
+        // subtiles D = 4w .. 4w+3 sit in fragments 2w, 2w+1 of each key subtile
+        lds_read_vt4<VF * 1024>(vb + vbase + 2048 * w, av);
+      } else {
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const int D = ND * w + d;                 // value subtile index
-        const int off = vbase + ((D >> 1) * 4 + 2 * (D & 1)) * 256;
-        const v4s lo = lds_read_tr16(vb, off);
-        const v4s hi = lds_read_tr16(vb, off + VF * 1024);
-        av[d] = (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int d = 0; d < ND; ++d) {
+          const int D = ND * w + d;                 // value subtile index
+          const int off = vbase + ((D >> 1) * 4 + 2 * (D & 1)) * 256;
+          const v4s lo = lds_read_tr16(vb, off);
+          const v4s hi = lds_read_tr16(vb, off + VF * 1024);
+          av[d] = (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
 #pragma unroll
       for (int hs = 0; hs < NW; ++hs) {
@@ -271,7 +359,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    lds_barrier();
   }
 
   // epilogue: row sums of every head, then lane (c, g) of wave w writes
@@ -441,9 +529,10 @@ bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int
   if (f32) return H >= 1 && H <= 64 && Dk >= 4 && Dk <= 128 && Dv >= 4 && Dv <= 128 && Dk % 4 == 0 && Dv % 4 == 0;
   if (H == 16 && Dk == 128 && Dv == 128) return true;
   if (H == 128 && Dk == 576 && Dv == 512) {
-    // two gathered tiles + P^T + the index row must fit in LDS
+    // two gathered tiles + P^T (+ partial S^T) + the index row must fit in LDS
     const size_t tile = (size_t)32 * (Dk / 8 + (sep_v ? Dv / 8 : 0)) * 16;
-    return 2 * tile + 8 * 1024 + (size_t)k * 4 <= kAttnLdsLimit;
+    const size_t xch = attn_ksplit((int)Dk, 8, sep_v) ? 8 * 2048 : 0;
+    return 2 * tile + 8 * 1024 + xch + (size_t)k * 4 <= kAttnLdsLimit;
   }
   return false;
 }
@@ -470,7 +559,7 @@ size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t 
 template <int DK, int DV, int NW, bool SEPV>
 static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
   constexpr size_t tile = (size_t)32 * (DK / 8 + (SEPV ? DV / 8 : 0)) * 16;
-  constexpr size_t fixed = 2 * tile + (size_t)NW * 1024;
+  constexpr size_t fixed = 2 * tile + (size_t)NW * 1024 + (attn_ksplit(DK, NW, SEPV) ? (size_t)NW * 2048 : 0);
   constexpr size_t lds_max = fixed + (size_t)DSA_MAX_TOPK * 4 <= kAttnLdsLimit
                                  ? fixed + (size_t)DSA_MAX_TOPK * 4 : kAttnLdsLimit;
   const size_t lds = fixed + (size_t)a.k * 4;

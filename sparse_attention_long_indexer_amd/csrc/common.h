@@ -148,4 +148,19 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global access (vmcnt(0)), which would stall on
+// direct-to-LDS gathers issued for later tiles; their completion is instead
+// awaited explicitly with s_waitcnt vmcnt before the barrier that publishes
+// the tile.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier; lgkmcnt(0) completes this wave's LDS accesses.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace dsa

@@ -95,6 +95,11 @@ def test_attn_validation(lib):
     assert f(*args(q=_vp(0x10008))) == 2           # misaligned Q
     assert f(*args(S=0)) == 2
     assert f(*args(T=0)) == 0
+    # bf16 rows are gathered through 32-bit byte offsets: S * ld * 2 <= 4 GiB
+    # (only failing cases here: a call that passes validation would launch)
+    assert f(*args(S=(1 << 32) // 256 + 1)) == 4
+    assert f(*args(S=(1 << 31) // 128 + 1, ldkv=256, v=None)) == 4
+    assert f(*args(S=(1 << 31) // 128 + 1, ldv=256)) == 4
 
 
 def test_forward_validation(lib):
