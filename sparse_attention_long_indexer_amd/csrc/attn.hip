@@ -93,7 +93,9 @@ __device__ __forceinline__ v4s lds_read_tr16(const char* lds_base, int byte_off)
 // av[d] = (key rows 0-15 | key rows 16-31).  One asm block that ends with
 // its own lgkmcnt wait: through the builtin, each read would also wait for
 // the direct-to-LDS gather of the next tile still in flight into the other
-// buffer, because the compiler cannot tell the two LDS regions apart.
+// buffer, because the compiler cannot tell the two LDS regions apart.  The
+// outputs are early-clobber: a load may land before a later one reads the
+// address register.
 template <int HI>
 __device__ __forceinline__ void lds_read_vt4(const char* lds_ptr, v8s* av) {
   const uint32_t addr = (uint32_t)(uintptr_t)(const lds_char*)lds_ptr;
@@ -108,7 +110,7 @@ __device__ __forceinline__ void lds_read_vt4(const char* lds_ptr, v8s* av) {
       "ds_read_b64_tr_b16 %6, %8 offset:%11\n\t"
       "ds_read_b64_tr_b16 %7, %8 offset:%12\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3), "=v"(r4), "=v"(r5), "=v"(r6), "=v"(r7)
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
       : "v"(addr), "i"(HI), "i"(HI + 512), "i"(HI + 1024), "i"(HI + 1536)
       : "memory");
   const v2i lo[4] = {r0, r1, r2, r3}, hi[4] = {r4, r5, r6, r7};
