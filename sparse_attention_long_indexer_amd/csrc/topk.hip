@@ -18,7 +18,7 @@
 // one block per row then selects exactly among the candidates.  When at
 // least m keys reach tau, the top m are all candidates, so the result is
 // exact; a row with too few or too many candidates (or a pathological tie)
-// is settled by the one-block-per-row select instead.
+// is settled by the same block with the full-row select instead.
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -69,7 +69,6 @@ constexpr int kCandMaxTies = 512;
 constexpr int64_t kCandMinN = 16384;    // shorter rows: one block per row is enough
 constexpr int64_t kCandMaxN = 524288;   // the bitmap of kept positions fits in LDS
 constexpr int64_t kCandMaxRows = 512;   // more rows fill the chip one block per row
-constexpr int kCandFbBlocks = 64;
 
 static bool topk_use_candidates(int64_t rows, int64_t max_n, int64_t k) {
   return rows >= 1 && rows < kCandMaxRows && max_n >= kCandMinN && max_n <= kCandMaxN && 2 * k <= kCandCap;
@@ -90,21 +89,17 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
 // min(1.75 m, (m + cap) / 2) keys of the row reach it.  0 (below every key)
 // when the whole row fits the candidate list.  A threshold on the zero
 // score is raised past it, so ReLU's zeros do not flood the list.  Also
-// clears the row's candidate count and (block 0) the fallback queue.
+// clears the row's candidate count.
 __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRows R, int64_t k,
                                                                          uint32_t* __restrict__ tau,
-                                                                         int32_t* __restrict__ cnt,
-                                                                         int32_t* __restrict__ fb) {
+                                                                         int32_t* __restrict__ cnt) {
   __shared__ uint32_t skey[kCandSample];
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t scan[kCandWaves];
   __shared__ uint32_t s_out[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t row = blockIdx.x;
-  if (tid == 0) {
-    cnt[row] = 0;
-    if (row == 0) fb[0] = 0;
-  }
+  if (tid == 0) cnt[row] = 0;
   const RowView rv = topk_row_view(R, row);
   const int64_t n = rv.n, m = n < k ? n : k;
   if (n <= kCandCap) {
@@ -209,21 +204,19 @@ __global__ __launch_bounds__(256) void topk_cand_filter_kernel(TopkRows R, const
 }
 
 // Exact top m of a row from its candidates (radix select in LDS, ascending
-// output through a bitmap of kept positions); rows the candidates cannot
-// settle go to the fallback queue fb.
-__global__ __launch_bounds__(kCandThreads) void topk_cand_select_kernel(TopkRows R, int64_t k,
+// output through a bitmap of kept positions); a row the candidates cannot
+// settle is selected from its full score row by the same block.
+__global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows R, int64_t k,
                                                                        const uint32_t* __restrict__ tau,
                                                                        const uint2* __restrict__ cand,
                                                                        const int32_t* __restrict__ cnt,
                                                                        int32_t* __restrict__ idx_out,
-                                                                       int32_t* __restrict__ count_out,
-                                                                       int32_t* __restrict__ fb) {
+                                                                       int32_t* __restrict__ count_out) {
+  constexpr int NT = kTopkThreads;
   extern __shared__ __align__(16) uint32_t sm[];
   uint2* cl = (uint2*)sm;                  // [kCandCap] (key, position)
   uint32_t* bitmap = sm + 2 * kCandCap;    // [nwords]
-  __shared__ uint32_t hist[1024];
-  __shared__ uint32_t wave_cnt[kCandWaves];
-  __shared__ uint32_t s_sel[2];
+  __shared__ TopkShared sh;
   __shared__ int32_t s_tie[kCandMaxTies];
   __shared__ int s_ntie;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -233,21 +226,21 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_select_kernel(TopkRows
   int32_t* o = idx_out + row * k;
   if (count_out && tid == 0) count_out[row] = (int32_t)m;
   if (n <= k) {
-    for (int64_t i = tid; i < k; i += kCandThreads) o[i] = i < n ? (int32_t)i : -1;
+    for (int64_t i = tid; i < k; i += NT) o[i] = i < n ? (int32_t)i : -1;
     return;
   }
   const uint32_t tk = tau[row];
   const int c = cnt[row];
-  if (c > kCandCap || (tk != 0u && c < m)) {
-    if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)row;
+  if (c > kCandCap || (tk != 0u && c < m)) {  // block-uniform
+    select_row(rv.p, n, k, o, sh);
     return;
   }
   const int nwords = (int)((n + 31) >> 5);
-  for (int i = tid; i < nwords; i += kCandThreads) bitmap[i] = 0u;
+  for (int i = tid; i < nwords; i += NT) bitmap[i] = 0u;
   if (tid == 0) s_ntie = 0;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   const uint2* cr = cand + row * kCandCap;
-  for (int e = tid; e < c; e += kCandThreads) {
+  for (int e = tid; e < c; e += NT) {
     const uint2 v = cr[e];
     cl[e] = v;
     mn = min(mn, v.x);
@@ -256,44 +249,31 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_select_kernel(TopkRows
   mn = wave_min(mn);
   mx = wave_max(mx);
   if (lane == 0) {
-    hist[w] = mn;
-    hist[kCandWaves + w] = mx;
+    sh.hist[w] = mn;
+    sh.hist[kTopkWaves + w] = mx;
   }
   __syncthreads();
   mn = 0xFFFFFFFFu;
   mx = 0u;
 #pragma unroll
-  for (int i = 0; i < kCandWaves; ++i) {
-    mn = min(mn, hist[i]);
-    mx = max(mx, hist[kCandWaves + i]);
+  for (int i = 0; i < kTopkWaves; ++i) {
+    mn = min(mn, sh.hist[i]);
+    mx = max(mx, sh.hist[kTopkWaves + i]);
   }
   __syncthreads();
   uint32_t thr, need;
-  radix_select<kCandThreads>([&](int64_t e) { return cl[e].x; }, c, (uint32_t)m, tk != 0u ? tk : mn, mx, hist,
-                             wave_cnt, s_sel, thr, need);
-  if (!output_from_candidates<kCandThreads>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie, kCandMaxTies,
-                                            &s_ntie, wave_cnt, o)) {
-    if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)row;
-  }
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_cand_fallback_kernel(TopkRows R, int64_t k,
-                                                                         const int32_t* __restrict__ fb,
-                                                                         int32_t* __restrict__ idx_out) {
-  __shared__ TopkShared sh;
-  const int nfb = fb[0];
-  for (int f = blockIdx.x; f < nfb; f += gridDim.x) {
-    const int64_t row = fb[1 + f];
-    const RowView rv = topk_row_view(R, row);
-    select_row(rv.p, rv.n, k, idx_out + row * k, sh);
+  radix_select<NT>([&](int64_t e) { return cl[e].x; }, c, (uint32_t)m, tk != 0u ? tk : mn, mx, sh.hist,
+                   sh.wave_cnt, sh.sel, thr, need);
+  if (!output_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie, kCandMaxTies, &s_ntie,
+                                  sh.wave_cnt, o)) {
     __syncthreads();
+    select_row(rv.p, n, k, o, sh);  // a boundary tie too long for the list
   }
 }
 
 struct CandWs {
   uint32_t* tau;
   int32_t* cnt;
-  int32_t* fb;
   uint2* cand;
 };
 
@@ -306,9 +286,8 @@ static size_t cand_layout(int64_t rows, char* base, CandWs* out) {
   };
   char* tau = take((size_t)rows * 4);
   char* cnt = take((size_t)rows * 4);
-  char* fb = take((size_t)(rows + 1) * 4);
   char* cand = take((size_t)rows * kCandCap * 8);
-  if (out) *out = CandWs{(uint32_t*)tau, (int32_t*)cnt, (int32_t*)fb, (uint2*)cand};
+  if (out) *out = CandWs{(uint32_t*)tau, (int32_t*)cnt, (uint2*)cand};
   return off;
 }
 
@@ -326,7 +305,7 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
   }
   CandWs c;
   cand_layout(rows, (char*)ws, &c);
-  topk_cand_estimate_kernel<<<(unsigned)rows, kCandThreads, 0, st>>>(r, k, c.tau, c.cnt, c.fb);
+  topk_cand_estimate_kernel<<<(unsigned)rows, kCandThreads, 0, st>>>(r, k, c.tau, c.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 fgrid((unsigned)((max_n + kCandSpan - 1) / kCandSpan), (unsigned)rows);
@@ -341,11 +320,8 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
     attr = true;
   }
   const size_t lds = (size_t)kCandCap * 8 + (size_t)((max_n + 31) / 32) * 4;
-  topk_cand_select_kernel<<<(unsigned)rows, kCandThreads, lds, st>>>(r, k, c.tau, c.cand, c.cnt, idx_out,
-                                                                     count_out, c.fb);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned fbb = (unsigned)(rows < kCandFbBlocks ? rows : kCandFbBlocks);
-  topk_cand_fallback_kernel<<<fbb, kTopkThreads, 0, st>>>(r, k, c.fb, idx_out);
+  topk_cand_select_kernel<<<(unsigned)rows, kTopkThreads, lds, st>>>(r, k, c.tau, c.cand, c.cnt, idx_out,
+                                                                     count_out);
   return hipGetLastError();
 }
 
