@@ -143,17 +143,19 @@ def attend(q_heads: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: f
 # ---------------------------------------------------------- whole forward ---
 
 class PrefillOracle:
-    """One causal prefill (queries = keys = L tokens).
+    """One causal prefill over S key tokens; query row t is the token at
+    position q_offset + t (q_offset = 0: queries = keys, the whole sequence;
+    q_offset > 0: the last T tokens, a later chunk of a long prefill).
 
     Arguments are host numpy arrays in the library's storage formats:
-      q_idx, k_idx : uint8 e4m3 codes [L,128] with fp32 scales [L]   (FP8)
-                     or float32 [L,128] with scales None              (fp32)
+      q_idx, k_idx : uint8 e4m3 codes [T,128] / [S,128] with fp32 scales
+                     (FP8), or float32 rows with scales None (fp32)
       w            : uint16 bf16 bits or float32 [128,128]
-      q            : [L,H,Dk] (uint16 bf16 bits or float32)
-      kv           : [L,Dk]; v : [L,Dv] or None (then V = kv[:, :Dv])
+      q            : [T,H,Dk] (uint16 bf16 bits or float32)
+      kv           : [S,Dk]; v : [S,Dv] or None (then V = kv[:, :Dv])
     """
 
-    def __init__(self, q_idx, q_scale, k_idx, k_scale, w, q, kv, v, topk, scale, Dv):
+    def __init__(self, q_idx, q_scale, k_idx, k_scale, w, q, kv, v, topk, scale, Dv, q_offset=0):
         self.fp8 = q_scale is not None
         if self.fp8:
             qv = dequant_rows(q_idx, q_scale)
@@ -172,12 +174,13 @@ class PrefillOracle:
             self.q_vals = self.qf
         self.q, self.kv, self.v = q, kv, v
         self.k, self.scale, self.Dv = topk, scale, Dv
+        self.q_offset = int(q_offset)
 
     def q_scale_of(self, t: int) -> float:
         return 1.0 if self.qf_scale is None else float(self.qf_scale[t])
 
     def scores_row(self, t: int) -> np.ndarray:
-        return index_scores_row(self.q_vals[t], self.q_scale_of(t), self.k_vals, self.k_scale, t)
+        return index_scores_row(self.q_vals[t], self.q_scale_of(t), self.k_vals, self.k_scale, self.q_offset + t)
 
     def select_row(self, t: int) -> np.ndarray:
         return topk_row(self.scores_row(t), self.k)

@@ -255,6 +255,25 @@ def pin_brute_force(od, oc):
             assert np.allclose(go, o, rtol=1e-12, atol=1e-14), (spec.name, t)
 
 
+def pin_prefill_chunk_brute_force(od, oc):
+    """A later chunk of a prefill (queries at positions q_offset.., keys the
+    whole prefix) gives the whole-sequence rows: checked against the brute
+    force of the whole sequence."""
+    for spec, seed, q0 in ((TINY_FP8, 4, 7), (TINY_MLA, 5, 4)):
+        x = gen.make_prefill(spec, seed=seed)
+        orc = od.PrefillOracle(_np(x["q_idx"][q0:]), _np(x["q_scale"][q0:]) if x["q_scale"] is not None else None,
+                               _np(x["k_idx"]), _np(x["k_scale"]), _np(x["w"]), _np(x["q"][q0:]), _np(x["kv"]),
+                               _np(x["v"]), spec.topk, spec.scale, spec.Dv, q_offset=q0)
+        rows = list(range(q0, spec.L))
+        bf = brute_force_prefill(spec, x, rows)
+        for t in rows:
+            sc, sel, o = bf[t]
+            assert np.allclose(orc.scores_row(t - q0), sc, rtol=1e-13, atol=0), (spec.name, t)
+            idx, go, _ = orc.row(t - q0)
+            assert list(idx[: len(sel)]) == sel and np.all(idx[len(sel):] == -1), (spec.name, t)
+            assert np.allclose(go, o, rtol=1e-12, atol=1e-14), (spec.name, t)
+
+
 def pin_scores_causal_relu(od, oc):
     spec = TINY_FP8.with_(L=40)
     x = gen.make_prefill(spec, seed=4)
@@ -398,6 +417,7 @@ def pin_page_constants(od, oc):
 ALL_PINS = [
     pin_e4m3_decode_matches_library, pin_e4m3_landmarks, pin_e4m3_encode_matches_library,
     pin_e4m3_encode_midpoints_and_saturation, pin_bf16_decode_matches_library, pin_fold_orientation,
-    pin_requant_closed_forms, pin_scores_one_hot, pin_brute_force, pin_scores_causal_relu, pin_topk_properties,
+    pin_requant_closed_forms, pin_scores_one_hot, pin_brute_force, pin_prefill_chunk_brute_force,
+    pin_scores_causal_relu, pin_topk_properties,
     pin_attend_special_cases, pin_sparse_equals_dense, pin_decode_equals_prefill_row, pin_page_constants,
 ]

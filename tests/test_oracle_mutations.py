@@ -143,7 +143,12 @@ def _bf16_wrong_shift(bits):
     return b.view(np.float32).astype(np.float64)
 
 
+def _chunk_ignores_offset(self, t):
+    return od.index_scores_row(self.q_vals[t], self.q_scale_of(t), self.k_vals, self.k_scale, t)
+
+
 MUTATIONS = {
+    "prefill_chunk_ignores_offset": (od.PrefillOracle, "scores_row", _chunk_ignores_offset),
     "fold_transposed": (od, "fold", _fold_transposed),
     "requant_wrong_constant": (od, "requant", _requant_wrong_const),
     "requant_scale_not_f32": (od, "requant", _requant_no_f32_round),
