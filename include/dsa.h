@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 #define DSA_INDEX_DIM 128   /* index-key width, write-up section 2.2 */
 #define DSA_MAX_TOPK 4096
 
@@ -168,14 +168,21 @@ dsa_status_t dsa_sparse_attn(const void* q, int64_t T, int64_t H, int64_t Dk, ds
 /*
  * Whole forward: fold, scores, top-k and sparse attention.
  *
- * PREFILL: T tokens of one causal sequence (queries = keys, pos(t) = t).
- *   q_idx/q_scale [T][128], k_idx/k_scale [T][128], q [T][H][Dk],
- *   kv [T][ld_kv], v [T][ld_v] or NULL; out [T][H][Dv]; idx_out [T][k].
+ * PREFILL: T query tokens at positions q_offset .. q_offset + T - 1 of one
+ *   causal sequence whose first S = q_offset + T tokens are the keys
+ *   (q_offset = 0: the whole sequence, queries = keys).  Query t attends
+ *   over keys [0, q_offset + t].  q_offset > 0 runs a long prefill in
+ *   chunks: each chunk reuses the keys cached by the earlier ones, and the
+ *   result equals the rows of the whole-sequence call.
+ *   q_idx/q_scale [T][128], k_idx/k_scale [S][128], q [T][H][Dk],
+ *   kv [S][ld_kv], v [S][ld_v] or NULL; out [T][H][Dv]; idx_out [T][k].
+ *   S <= 2^31 - 1.
  * DECODE: B sequences, one new query each.  Sequence b owns cache rows
  *   [seq_offsets[b], seq_offsets[b+1]) of k_idx/k_scale/kv/v (device int64
  *   [B+1], non-decreasing, seq_offsets[0] = 0, every length >= 1); its
  *   query sits at position n_b - 1 and attends over keys [0, n_b) of its
- *   own cache.  q_idx/q_scale [B][128], q [B][H][Dk]; out [B][H][Dv];
+ *   own cache.  q_offset must be 0.
+ *   q_idx/q_scale [B][128], q [B][H][Dk]; out [B][H][Dv];
  *   idx_out [B][k] holds indices local to each sequence's cache.
  *   max_len is an upper bound on every n_b (host value, used to size work;
  *   BF16 attention needs max_len * ld * 2 <= 4 GiB, as for dsa_sparse_attn).
@@ -205,6 +212,7 @@ typedef struct dsa_forward_args {
   int64_t ld_v;
   int64_t topk;
   float scale;
+  int64_t q_offset;           /* PREFILL: position of the first query */
 } dsa_forward_args;
 
 size_t dsa_forward_workspace_size(const dsa_forward_args* a);

@@ -24,6 +24,7 @@ DSA_FLAG_FUSED = 2
 DSA_FLAG_FORCE_FALLBACK = 4
 INDEX_DIM = 128
 MAX_TOPK = 4096
+ABI_VERSION = 2
 
 EXPORTED = [
     "dsa_abi_version", "dsa_status_str", "dsa_fold_index_query", "dsa_index_scores",
@@ -47,7 +48,7 @@ class ForwardArgs(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("attn_dtype", ctypes.c_int), ("q", ctypes.c_void_p),
         ("H", ctypes.c_int64), ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64), ("kv", ctypes.c_void_p),
         ("ld_kv", ctypes.c_int64), ("v", ctypes.c_void_p), ("ld_v", ctypes.c_int64),
-        ("topk", ctypes.c_int64), ("scale", ctypes.c_float),
+        ("topk", ctypes.c_int64), ("scale", ctypes.c_float), ("q_offset", ctypes.c_int64),
     ]
 
 
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = res
+    if lib.dsa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI {lib.dsa_abi_version()}, this binding expects {ABI_VERSION}: rebuild it")
     return lib
 
 
@@ -172,9 +175,11 @@ def dsa_sparse_attn(q, kv, idx, scale, v=None, Dv=None, out=None, lse_out=None, 
 
 
 def forward_args(x: dict, topk: int, scale: float, Dv: int, mode: int = DSA_MODE_PREFILL, flags: int = 0,
-                 max_len: int = 0):
+                 max_len: int = 0, q_offset: int = 0):
     """Build the dsa_forward argument struct from an input dict of device
-    tensors (keys as produced by the input generators)."""
+    tensors (keys as produced by the input generators).  For a prefill chunk
+    (q_offset > 0) the query tensors hold the chunk's rows and the key
+    tensors the first q_offset + T rows of the sequence."""
     q = x["q"]
     a = ForwardArgs()
     a.mode = mode
@@ -197,6 +202,7 @@ def forward_args(x: dict, topk: int, scale: float, Dv: int, mode: int = DSA_MODE
     a.ld_v = v.stride(0) if v is not None else 0
     a.topk = topk
     a.scale = scale
+    a.q_offset = q_offset
     if mode == DSA_MODE_DECODE:
         a.seq_offsets = x["offsets"].data_ptr()
         a.total_keys = x["k_idx"].shape[0]

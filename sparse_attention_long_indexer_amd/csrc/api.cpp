@@ -102,10 +102,13 @@ struct FwdPlan {
 
 constexpr int64_t kFusedMinT = 4096;  // shorter prefills materialise their scores
 
+// keys a prefill chunk sees: the chunk's T queries are the last T of them
+int64_t prefill_keys(const dsa_forward_args* a) { return a->q_offset + a->T; }
+
 bool use_fused(const dsa_forward_args* a) {
   return a->mode == DSA_MODE_PREFILL && a->idx_dtype == DSA_FP8_E4M3 &&
-         !(a->flags & DSA_FLAG_MATERIALIZE) && index_select_supported(a->T, a->T) &&
-         (a->T >= kFusedMinT || (a->flags & DSA_FLAG_FUSED));
+         !(a->flags & DSA_FLAG_MATERIALIZE) && index_select_supported(a->T, prefill_keys(a)) &&
+         (prefill_keys(a) >= kFusedMinT || (a->flags & DSA_FLAG_FUSED));
 }
 
 constexpr size_t kAlign = 256;
@@ -126,9 +129,9 @@ FwdPlan plan_forward(const dsa_forward_args* a, bool need_idx) {
   p.fused = use_fused(a);
   if (p.fused) {
     p.chunk_rows = R;
-    off = round_up(off + index_select_workspace_bytes(a->T, a->T), kAlign);
+    off = round_up(off + index_select_workspace_bytes(a->T, prefill_keys(a)), kAlign);
   } else if (a->mode == DSA_MODE_PREFILL) {
-    const int64_t S = a->T;
+    const int64_t S = prefill_keys(a);
     int64_t rows = S > 0 ? (int64_t)(kScoreChunkBytes / ((size_t)S * 4)) : 1;
     rows = rows / 64 * 64;
     if (rows < 64) rows = 64;
@@ -151,12 +154,14 @@ dsa_status_t check_forward(const dsa_forward_args* a) {
   if (!a) return DSA_ERR_NULL;
   if (a->mode != DSA_MODE_PREFILL && a->mode != DSA_MODE_DECODE) return DSA_ERR_UNSUPPORTED;
   if (a->T < 0 || a->topk < 1 || a->topk > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+  if (a->q_offset < 0 || (a->mode == DSA_MODE_DECODE && a->q_offset != 0)) return DSA_ERR_SHAPE;
+  if (a->mode == DSA_MODE_PREFILL && a->q_offset > (int64_t(1) << 31) - 1 - a->T) return DSA_ERR_SHAPE;
   if (a->mode == DSA_MODE_DECODE) {
     if (a->idx_dtype != DSA_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
     if (a->total_keys < a->T || a->max_len < 1) return DSA_ERR_SHAPE;
     if (a->T > 0 && !a->seq_offsets) return DSA_ERR_NULL;
   }
-  const int64_t S = a->mode == DSA_MODE_PREFILL ? a->T : a->total_keys;
+  const int64_t S = a->mode == DSA_MODE_PREFILL ? prefill_keys(a) : a->total_keys;
   DSA_TRY(check_fold(a->q_idx, a->q_scale, a->idx_dtype, a->w_index, a->w_dtype, a->T, a->q_idx,
                      a->q_scale));
   if (a->T > 0) {
@@ -214,7 +219,7 @@ dsa_status_t dsa_index_scores(const void* qf, const float* qf_scale, const void*
     if (row_end == row_begin || S == 0) return DSA_OK;
     DSA_TRY(check_device());
     return from_hip(launch_index_scores(qf, qf_scale, k_idx, k_scale, idx_dtype == DSA_FP8_E4M3, T,
-                                        S, q_pos, row_begin, row_end, scores_out, ld,
+                                        S, q_pos, 0, row_begin, row_end, scores_out, ld,
                                         as_stream(stream)));
   } catch (...) {
     return DSA_ERR_DEVICE;
@@ -235,7 +240,7 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t S, con
     const size_t need = topk_workspace_bytes(T, S, k);
     if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
     DSA_TRY(check_device());
-    TopkRows r{scores, ld, nullptr, q_pos, S, nullptr, 0};
+    TopkRows r{scores, ld, nullptr, q_pos, S, nullptr, 0, 0};
     return from_hip(launch_topk(r, T, S, k, idx_out, count_out, ws, as_stream(stream)));
   } catch (...) {
     return DSA_ERR_DEVICE;
@@ -328,18 +333,20 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
     at.lse = nullptr;
 
     if (p.fused) {
-      e = launch_index_select((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale, R, R, a->topk, idx,
+      const int64_t S = prefill_keys(a);
+      e = launch_index_select((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale, R, S, a->topk, idx,
                               sc, (a->flags & DSA_FLAG_FORCE_FALLBACK) != 0, st);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
       at.seq_offsets = nullptr;
-      at.S = R;
+      at.S = S;
     } else if (a->mode == DSA_MODE_PREFILL) {
-      const int64_t S = R;
+      const int64_t S = prefill_keys(a);
       for (int64_t r0 = 0; r0 < R; r0 += p.chunk_rows) {
         const int64_t r1 = r0 + p.chunk_rows < R ? r0 + p.chunk_rows : R;
-        e = launch_index_scores(qf, qs, a->k_idx, a->k_scale, fp8, R, S, nullptr, r0, r1, sc, S, st);
+        e = launch_index_scores(qf, qs, a->k_idx, a->k_scale, fp8, R, S, nullptr, a->q_offset, r0, r1, sc, S,
+                                st);
         if (e != hipSuccess) return DSA_ERR_DEVICE;
-        TopkRows tr{sc, S, nullptr, nullptr, S, nullptr, r0};
+        TopkRows tr{sc, S, nullptr, nullptr, S, nullptr, r0, a->q_offset};
         e = launch_topk(tr, r1 - r0, S, a->topk, idx + r0 * a->topk, nullptr, nullptr, st);
         if (e != hipSuccess) return DSA_ERR_DEVICE;
       }
@@ -349,7 +356,7 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
       e = launch_index_scores_decode((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale,
                                      a->seq_offsets, R, a->max_len, sc, st);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
-      TopkRows tr{sc, 0, nullptr, nullptr, 0, a->seq_offsets, 0};
+      TopkRows tr{sc, 0, nullptr, nullptr, 0, a->seq_offsets, 0, 0};
       e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, p.topk_bytes ? base + p.topk_off : nullptr, st);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
       at.seq_offsets = a->seq_offsets;

@@ -22,7 +22,7 @@ constexpr int kKeysPerBlock = 128;  // 8 MFMA tiles per wave
 
 __global__ __launch_bounds__(256) void index_scores_fp8_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k,
-    const float* __restrict__ ks, int64_t S, const int64_t* __restrict__ q_pos, int64_t row_begin,
+    const float* __restrict__ ks, int64_t S, const int64_t* __restrict__ q_pos, int64_t pos_base, int64_t row_begin,
     int64_t row_end, float* __restrict__ out, int64_t ld) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void index_scores_fp8_kernel(
     rok[i] = r < row_end;
     const int64_t rr = rok[i] ? r : row_end - 1;
     qsc[i] = qs[rr];
-    pos[i] = q_pos ? q_pos[rr] : rr;
+    pos[i] = q_pos ? q_pos[rr] : pos_base + rr;
   }
 #pragma unroll 2
   for (int j = 0; j < kKeysPerBlock / 16; ++j) {
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void index_scores_fp8_kernel(
 // fp32 operands (no quantisation): one thread per score, sequential fp32 FMA.
 __global__ __launch_bounds__(256) void index_scores_f32_kernel(
     const float* __restrict__ qf, const float* __restrict__ k, int64_t S,
-    const int64_t* __restrict__ q_pos, int64_t row_begin, int64_t row_end, float* __restrict__ out,
+    const int64_t* __restrict__ q_pos, int64_t pos_base, int64_t row_begin, int64_t row_end, float* __restrict__ out,
     int64_t ld) {
   __shared__ float qt[16][kIdxDim + 1];
   __shared__ float kt[16][kIdxDim + 1];
@@ -87,12 +87,12 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(
   float acc = 0.f;
 #pragma unroll 8
   for (int j = 0; j < kIdxDim; ++j) acc = fmaf(qt[ty][j], kt[tx][j], acc);
-  const int64_t p = q_pos ? q_pos[r] : r;
+  const int64_t p = q_pos ? q_pos[r] : pos_base + r;
   out[(r - row_begin) * ld + s] = (s <= p) ? (acc > 0.f ? acc : 0.f) : -INFINITY;
 }
 
 hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, const float* ks,
-                               bool fp8, int64_t T, int64_t S, const int64_t* q_pos,
+                               bool fp8, int64_t T, int64_t S, const int64_t* q_pos, int64_t pos_base,
                                int64_t row_begin, int64_t row_end, float* out, int64_t ld,
                                hipStream_t st) {
   (void)T;
@@ -102,11 +102,11 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
     dim3 grid((unsigned)((S + kKeysPerBlock - 1) / kKeysPerBlock),
               (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     index_scores_fp8_kernel<<<grid, 256, 0, st>>>((const uint8_t*)qf, qs, (const uint8_t*)k, ks, S,
-                                                   q_pos, row_begin, row_end, out, ld);
+                                                   q_pos, pos_base, row_begin, row_end, out, ld);
   } else {
     dim3 grid((unsigned)((S + 15) / 16), (unsigned)((rows + 15) / 16));
     index_scores_f32_kernel<<<grid, 256, 0, st>>>((const float*)qf, (const float*)k, S, q_pos,
-                                                   row_begin, row_end, out, ld);
+                                                   pos_base, row_begin, row_end, out, ld);
   }
   return hipGetLastError();
 }

@@ -26,6 +26,7 @@
 // Every path uses the same fp32 score u = fl(fl(acc * ks) * qs), so the
 // output equals the materialised scores + top-k path bit for bit.
 #include "common.h"
+#include "dsa.h"
 #include "kernels.h"
 #include "select.h"
 
@@ -36,6 +37,7 @@ constexpr int kCap = 1536;                 // survivors per segment
 constexpr int kTakeAll = 5632;             // rows this short keep every key
 constexpr int kSampleMax = 4096;           // samples per row (max)
 constexpr float kAlpha = 1.75f;            // survivor target / m
+constexpr int64_t kSelBitmapN = 262144;    // longer rows emit their indices by sorting, not via a bitmap
 
 __host__ __device__ inline int sample_stride(int64_t S) {
   int p = 32;
@@ -72,9 +74,10 @@ __global__ __launch_bounds__(kEstWaves * 64) void idx_estimate_kernel(const uint
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int64_t R0 = (int64_t)blockIdx.x * 16;
+  const int64_t p0 = S - T;  // position of row 0
   const int64_t rlast = min(R0 + 15, T - 1);
   const int P = sample_stride(S);
-  const int64_t nsb = samples_upto(min(rlast, S - 1), P);  // samples any row of the block uses
+  const int64_t nsb = samples_upto(min(p0 + rlast, S - 1), P);  // samples any row of the block uses
 
   const v8i a = *(const v8i*)(qf + min(R0 + c, T - 1) * kIdxDim + 32 * g);
   float qsc[4];
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kEstWaves * 64) void idx_estimate_kernel(const uint
     const int row = (16 / kEstWaves) * w + rr;
     const int64_t t = R0 + row;
     if (t >= T) break;
-    const int64_t n = min(t + 1, S);
+    const int64_t n = min(p0 + t + 1, S);
     const int64_t m = min(topk, n);
     if (n <= kTakeAll) {
       if (lane == 0) tau[t] = -INFINITY;
@@ -195,16 +198,26 @@ constexpr int kSegStride = kCap + kSlack;
 // Work items: long row blocks (keys past the chunk boundary kmax) are split
 // into chunk 0 = keys [0, kmax) and chunk 1 = keys [kmax, end), each with its
 // own survivor set, so no item scans more than kmax keys.  Items are ordered
-// longest first.
+// longest first.  Row block rb holds rows [256 rb, 256 rb + 256) at
+// positions p0 + row (p0 = S - T) and sees keys [0, min(S, p0 + 256 (rb+1))).
 struct FilterItem {
   int64_t rb;    // row block
   int set;       // key chunk / survivor set
   int64_t k0, k1;
 };
-__device__ __forceinline__ FilterItem filter_item(int64_t id, int64_t T, int64_t S, int64_t kmax) {
+__host__ __device__ inline int64_t filter_kmax(int64_t S) {
+  const int64_t h = (S + 1) / 2;
+  return (h + kFiltRows - 1) / kFiltRows * kFiltRows;
+}
+// first row block whose key range passes kmax
+__host__ __device__ inline int64_t filter_first_long(int64_t T, int64_t S) {
+  const int64_t kmax = filter_kmax(S), p0 = S - T;
+  return kmax >= p0 ? (kmax - p0) / kFiltRows : 0;
+}
+__device__ __forceinline__ FilterItem filter_item(int64_t id, int64_t T, int64_t S) {
   const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
-  // row blocks whose key range passes kmax
-  const int64_t first_long = kmax / kFiltRows;  // block rb sees keys < min(T, (rb+1)*256)
+  const int64_t kmax = filter_kmax(S), p0 = S - T;
+  const int64_t first_long = filter_first_long(T, S);
   const int64_t nl = nb > first_long ? nb - first_long : 0;
   FilterItem it;
   if (id < nl) {
@@ -217,7 +230,7 @@ __device__ __forceinline__ FilterItem filter_item(int64_t id, int64_t T, int64_t
     it.rb = nb - 1 - (id - nl);
     it.set = 0;
   }
-  const int64_t end = min(S, min(T, (it.rb + 1) * kFiltRows));
+  const int64_t end = min(S, p0 + (it.rb + 1) * kFiltRows);
   if (it.rb >= first_long) {
     it.k0 = it.set ? kmax : 0;
     it.k1 = it.set ? end : min(end, kmax);
@@ -227,13 +240,9 @@ __device__ __forceinline__ FilterItem filter_item(int64_t id, int64_t T, int64_t
   }
   return it;
 }
-__host__ __device__ inline int64_t filter_kmax(int64_t T) {
-  const int64_t h = (T + 1) / 2;
-  return (h + kFiltRows - 1) / kFiltRows * kFiltRows;
-}
-inline int64_t filter_items(int64_t T) {
+inline int64_t filter_items(int64_t T, int64_t S) {
   const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
-  const int64_t first_long = filter_kmax(T) / kFiltRows;
+  const int64_t first_long = filter_first_long(T, S);
   return nb + (nb > first_long ? nb - first_long : 0);
 }
 
@@ -245,9 +254,10 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
   __shared__ __align__(16) float kst[2][kFiltKeys];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const FilterItem item = filter_item(blockIdx.x, T, S, filter_kmax(T));
+  const FilterItem item = filter_item(blockIdx.x, T, S);
   const int64_t R0 = item.rb * kFiltRows;
-  const int64_t Q0 = R0 + 64 * w;
+  const int64_t Q0 = R0 + 64 * w;   // the wave's first row
+  const int64_t P0 = S - T + Q0;    // ... and its position
 
   v8i bq[4];
   int tq[4];
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
     const bool ok = t < T;
     const int64_t tt = ok ? t : T - 1;
     bq[q] = *(const v8i*)(qf + tt * kIdxDim + 32 * g);
-    tq[q] = ok ? (int)t : -1;  // an invalid query masks every key
+    tq[q] = ok ? (int)(S - T + t) : -1;  // key bound (position); an invalid query masks every key
     const float ta = tau[tt];
     // survivors need v * qs >= tau; shave a few ulps so rounding of the
     // product can never drop a key whose final score reaches tau
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
         cnt[q] = kCap;
       }
     }
-    const bool mask = kb + kFiltKeys - 1 > Q0;  // some key may lie past a query of this wave
+    const bool mask = kb + kFiltKeys - 1 > P0;  // some key may lie past a query of this wave
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int k16 = (int)(kb + 16 * kt);
@@ -360,13 +370,14 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  const bool two = item.rb >= filter_kmax(T) / kFiltRows;
+  const bool two = item.rb >= filter_first_long(T, S);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (tq[q] < 0) continue;
+    const int64_t t = Q0 + 16 * q + c;  // the row (tq holds its position)
     const int v = (ovf[q] || cnt[q] > (uint32_t)kCap) ? kCap + 1 : (int)cnt[q];
-    cnt_out[((int64_t)tq[q] * kSets + item.set) * kSeg + g] = v;
-    if (!two) cnt_out[((int64_t)tq[q] * kSets + 1) * kSeg + g] = 0;  // rows with one key chunk
+    cnt_out[(t * kSets + item.set) * kSeg + g] = v;
+    if (!two) cnt_out[(t * kSets + 1) * kSeg + g] = 0;  // rows with one key chunk
   }
 }
 
@@ -384,16 +395,16 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
     int32_t* __restrict__ fb, int force_fallback) {
   extern __shared__ __align__(16) uint32_t sm[];
   uint2* cl = (uint2*)sm;                       // [kSelMax] (score key, position) pairs
-  uint32_t* sel = sm + 2 * kSelMax;             // [nwords] bitmap of kept positions
+  uint32_t* sel = sm + 2 * kSelMax;             // [nwords] bitmap of kept positions (or a long row's sort buffer)
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t wave_cnt[kSelWaves];
   __shared__ uint32_t s_sel[2];
   __shared__ int s_cnt[kSets * kSeg], s_cbase[kSets * kSeg + 1];
   __shared__ int32_t s_tie[kMaxTies];
-  __shared__ int s_ntie, s_bad;
+  __shared__ int s_ntie, s_bad, s_nbuf;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t = blockIdx.x;
-  const int64_t n = min(t + 1, S);
+  const int64_t n = min(S - T + t + 1, S);
   const int64_t m = min(topk, n);
   int32_t* o = idx_out + t * topk;
   if (n <= topk) {
@@ -402,9 +413,13 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   }
   const float qsc = qs[t];
   const float tt = tau[t];
-  const int nwords = (int)((n + 31) >> 5);
+  const bool sorted = n > kSelBitmapN;
+  const int nwords = sorted ? 0 : (int)((n + 31) >> 5);
   if (tid < kSets * kSeg) s_cnt[tid] = cnt_in[t * kSets * kSeg + tid];
-  if (tid == 0) s_ntie = 0;
+  if (tid == 0) {
+    s_ntie = 0;
+    s_nbuf = 0;
+  }
   for (int i = tid; i < nwords; i += kSelThreads) sel[i] = 0;
   __syncthreads();
   // chunk layout: segment gq owns chunks [s_cbase[gq], s_cbase[gq+1])
@@ -497,8 +512,12 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
                             s_sel, thr, need);
   // keys above the m-th best go to the bitmap, ties to a list; a
   // pathological tie at the boundary is settled exactly elsewhere
-  if (!output_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel, nwords, s_tie, kMaxTies,
-                                           &s_ntie, wave_cnt, o)) {
+  const bool ok = sorted ? output_sorted_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk,
+                                                                      (int32_t*)sel, &s_nbuf, s_tie, kMaxTies,
+                                                                      &s_ntie, o)
+                          : output_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel, nwords,
+                                                                s_tie, kMaxTies, &s_ntie, wave_cnt, o);
+  if (!ok) {
     if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
   }
 }
@@ -508,7 +527,7 @@ constexpr int kFbBlocks = 64;
 
 __global__ __launch_bounds__(kTopkThreads) void idx_fallback_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
-    const float* __restrict__ ks, int64_t S, int64_t topk, const int32_t* __restrict__ fb,
+    const float* __restrict__ ks, int64_t S, int64_t p0, int64_t topk, const int32_t* __restrict__ fb,
     float* __restrict__ scratch, int32_t* __restrict__ idx_out) {
   __shared__ TopkShared sh;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -517,7 +536,7 @@ __global__ __launch_bounds__(kTopkThreads) void idx_fallback_kernel(
   float* row = scratch + (int64_t)blockIdx.x * S;
   for (int f = blockIdx.x; f < nfb; f += gridDim.x) {
     const int64_t t = fb[1 + f];
-    const int64_t n = min(t + 1, S);
+    const int64_t n = min(p0 + t + 1, S);
     const v8i a = *(const v8i*)(qf + t * kIdxDim + 32 * g);
     const float qsc = qs[t];
     for (int64_t s0 = (int64_t)w * 16; s0 < n; s0 += kTopkWaves * 16) {
@@ -549,7 +568,7 @@ size_t index_select_workspace_bytes(int64_t T, int64_t S) {
   return b;
 }
 
-bool index_select_supported(int64_t T, int64_t S) { return T == S && T <= 262144 && T >= 1; }
+bool index_select_supported(int64_t T, int64_t S) { return T >= 1 && S >= T && S <= (int64_t(1) << 31) - 1; }
 
 hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t* k8, const float* ks,
                                int64_t T, int64_t S, int64_t topk, int32_t* idx_out, void* ws,
@@ -571,21 +590,23 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
   if (e != hipSuccess) return e;
   idx_estimate_kernel<<<(unsigned)((T + 15) / 16), kEstWaves * 64, 0, st>>>(qf, qs, k8, ks, T, S, topk, tau);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  idx_filter_kernel<<<(unsigned)filter_items(T), 256, 0, st>>>(qf, qs, k8, ks, T, S, tau, cand, cnt);
+  idx_filter_kernel<<<(unsigned)filter_items(T, S), 256, 0, st>>>(qf, qs, k8, ks, T, S, tau, cand, cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int nwords = (int)((S + 31) / 32);
-  const size_t lds = (size_t)2 * kSelMax * 4 + (size_t)nwords * 4;
+  // bitmap words of the longest row with a bitmap, or the sort buffer
+  const int64_t bn = S < kSelBitmapN ? S : kSelBitmapN;
+  const int64_t words = (bn + 31) / 32 > DSA_MAX_TOPK ? (bn + 31) / 32 : DSA_MAX_TOPK;
+  const size_t lds = (size_t)2 * kSelMax * 4 + (size_t)words * 4;
   static bool attr = false;
   if (!attr) {
     e = hipFuncSetAttribute((const void*)idx_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(2 * kSelMax * 4 + (262144 / 32) * 4));
+                            (int)(2 * kSelMax * 4 + (kSelBitmapN / 32) * 4));
     if (e != hipSuccess) return e;
     attr = true;
   }
   idx_select_kernel<<<(unsigned)T, kSelThreads, lds, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, fb,
                                                           force_fallback ? 1 : 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  idx_fallback_kernel<<<kFbBlocks, kTopkThreads, 0, st>>>(qf, qs, k8, ks, S, topk, fb, scratch, idx_out);
+  idx_fallback_kernel<<<kFbBlocks, kTopkThreads, 0, st>>>(qf, qs, k8, ks, S, S - T, topk, fb, scratch, idx_out);
   return hipGetLastError();
 }
 

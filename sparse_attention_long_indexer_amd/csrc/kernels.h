@@ -12,9 +12,10 @@ namespace dsa {
 hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, const void* w,
                        bool w_bf16, int64_t T, void* q_out, float* s_out, hipStream_t st);
 
-// index_scores.hip: materialised scores for rows [row_begin, row_end)
+// index_scores.hip: materialised scores for rows [row_begin, row_end); row
+// t sits at position q_pos[t], or pos_base + t without q_pos
 hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, const float* ks,
-                               bool fp8, int64_t T, int64_t S, const int64_t* q_pos,
+                               bool fp8, int64_t T, int64_t S, const int64_t* q_pos, int64_t pos_base,
                                int64_t row_begin, int64_t row_end, float* out, int64_t ld,
                                hipStream_t st);
 // decode: scores of query b over its own cache rows, written at key offsets
@@ -31,12 +32,14 @@ struct TopkRows {
   int64_t S;                  // keys available (prefill) when seq_len == nullptr
   const int64_t* seq_offsets; // decode: n_b = off[b+1]-off[b], start = off[b]
   int64_t row_begin;          // first row (for q_pos lookup / output row)
+  int64_t pos_base;           // without q_pos, row t sits at position pos_base + t
 };
 size_t topk_workspace_bytes(int64_t rows, int64_t max_n, int64_t k);
 hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k, int32_t* idx_out,
                        int32_t* count_out, void* ws, hipStream_t st);
 
-// index_select.hip: fused scores + top-k for causal prefill (queries = keys)
+// index_select.hip: fused scores + top-k for a causal prefill chunk: query t
+// sits at position p0 + t and sees keys [0, p0 + t]; S = p0 + T keys
 bool index_select_supported(int64_t T, int64_t S);
 size_t index_select_workspace_bytes(int64_t T, int64_t S);
 hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t* k8, const float* ks,

@@ -48,7 +48,6 @@ template <int NT, class KeyAt>
 __device__ inline void radix_select(KeyAt key_at, int64_t n, uint32_t m, uint32_t lo, uint32_t hi,
                                     uint32_t* hist, uint32_t* scan, uint32_t* s_out, uint32_t& thr,
                                     uint32_t& need) {
-  constexpr int NW = NT / 64;
   constexpr int BINS = 1024, PER = BINS / NT > 0 ? BINS / NT : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t span = hi - lo;
@@ -238,6 +237,65 @@ __device__ inline bool output_from_candidates(const uint2* cl, int nslots, uint3
     }
   }
   for (int64_t i = m + tid; i < topk; i += NT) o[i] = -1;
+  return true;
+}
+
+// The same output without a bitmap, for rows too long for one in LDS: the m
+// kept positions (keys above thr, then the `need` lowest-position keys equal
+// to thr) are gathered into buf (LDS, at least the next power of two >= m
+// entries) and sorted ascending with a block-wide bitonic sort.  *s_nbuf and
+// *s_ntie must be zeroed by the caller before a barrier.  Returns false, with
+// nothing written to o, when the tie list overflows.
+template <int NT>
+__device__ inline bool output_sorted_from_candidates(const uint2* cl, int nslots, uint32_t thr, uint32_t need,
+                                                     int64_t n, int64_t m, int64_t topk, int32_t* buf,
+                                                     int* s_nbuf, int32_t* tie, int max_ties, int* s_ntie,
+                                                     int32_t* __restrict__ o) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < nslots; e += NT) {
+    const uint2 cv = cl[e];
+    const uint32_t key = cv.x;
+    const int32_t p = (int32_t)cv.y;
+    if (key < thr || p < 0 || p >= n) continue;
+    if (key > thr) {
+      buf[atomicAdd(s_nbuf, 1)] = p;
+    } else {
+      const int q = atomicAdd(s_ntie, 1);
+      if (q < max_ties) tie[q] = p;
+    }
+  }
+  __syncthreads();
+  const int ntie = *s_ntie;
+  if (ntie > max_ties) return false;
+  for (int i = tid; i < ntie; i += NT) {
+    const int32_t p = tie[i];
+    int rank = 0;
+    for (int j = 0; j < ntie; ++j) rank += tie[j] < p ? 1 : 0;
+    if (rank < (int)need) buf[atomicAdd(s_nbuf, 1)] = p;
+  }
+  __syncthreads();
+  const int cnt = *s_nbuf;  // == m
+  int len = 1;
+  while (len < cnt) len <<= 1;
+  for (int i = cnt + tid; i < len; i += NT) buf[i] = 0x7FFFFFFF;
+  __syncthreads();
+  for (int k = 2; k <= len; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < len; i += NT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const int32_t x = buf[i], y = buf[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            buf[i] = y;
+            buf[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int64_t i = tid; i < topk; i += NT) o[i] = i < m ? buf[i] : -1;
   return true;
 }
 

@@ -39,7 +39,7 @@ __device__ __forceinline__ RowView topk_row_view(const TopkRows& R, int64_t row)
     v.n = R.seq_offsets[row + 1] - lo;
   } else {
     const int64_t t = R.row_begin + row;
-    const int64_t pos = R.q_pos ? R.q_pos[t] : t;
+    const int64_t pos = R.q_pos ? R.q_pos[t] : R.pos_base + t;
     int64_t n = pos + 1 < R.S ? pos + 1 : R.S;
     v.n = n > 0 ? n : 0;
     v.p = R.scores + (R.row_off ? R.row_off[row] : row * R.ld);
@@ -67,11 +67,12 @@ constexpr int kCandThreads = 512;
 constexpr int kCandWaves = kCandThreads / 64;
 constexpr int kCandMaxTies = 512;
 constexpr int64_t kCandMinN = 16384;    // shorter rows: one block per row is enough
-constexpr int64_t kCandMaxN = 524288;   // the bitmap of kept positions fits in LDS
+constexpr int64_t kCandBitmapN = 524288;  // rows up to this long: ascending output via an LDS bitmap
+constexpr int kCandSortBuf = kCandCap / 2;  // longer rows: the kept positions (m <= cap / 2) sorted in LDS
 constexpr int64_t kCandMaxRows = 512;   // more rows fill the chip one block per row
 
 static bool topk_use_candidates(int64_t rows, int64_t max_n, int64_t k) {
-  return rows >= 1 && rows < kCandMaxRows && max_n >= kCandMinN && max_n <= kCandMaxN && 2 * k <= kCandCap;
+  return rows >= 1 && rows < kCandMaxRows && max_n >= kCandMinN && 2 * k <= kCandCap;
 }
 
 // integer hash (the "lowbias32" mixer) for window offsets
@@ -215,10 +216,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
   constexpr int NT = kTopkThreads;
   extern __shared__ __align__(16) uint32_t sm[];
   uint2* cl = (uint2*)sm;                  // [kCandCap] (key, position)
-  uint32_t* bitmap = sm + 2 * kCandCap;    // [nwords]
+  uint32_t* bitmap = sm + 2 * kCandCap;    // [nwords], or the sort buffer of a long row
   __shared__ TopkShared sh;
   __shared__ int32_t s_tie[kCandMaxTies];
-  __shared__ int s_ntie;
+  __shared__ int s_ntie, s_nbuf;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t row = blockIdx.x;
   const RowView rv = topk_row_view(R, row);
@@ -235,9 +236,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
     select_row(rv.p, n, k, o, sh);
     return;
   }
-  const int nwords = (int)((n + 31) >> 5);
+  const bool sorted = n > kCandBitmapN;
+  const int nwords = sorted ? 0 : (int)((n + 31) >> 5);
   for (int i = tid; i < nwords; i += NT) bitmap[i] = 0u;
-  if (tid == 0) s_ntie = 0;
+  if (tid == 0) {
+    s_ntie = 0;
+    s_nbuf = 0;
+  }
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   const uint2* cr = cand + row * kCandCap;
   for (int e = tid; e < c; e += NT) {
@@ -264,8 +269,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
   uint32_t thr, need;
   radix_select<NT>([&](int64_t e) { return cl[e].x; }, c, (uint32_t)m, tk != 0u ? tk : mn, mx, sh.hist,
                    sh.wave_cnt, sh.sel, thr, need);
-  if (!output_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie, kCandMaxTies, &s_ntie,
-                                  sh.wave_cnt, o)) {
+  const bool ok = sorted ? output_sorted_from_candidates<NT>(cl, c, thr, need, n, m, k, (int32_t*)bitmap, &s_nbuf,
+                                                             s_tie, kCandMaxTies, &s_ntie, o)
+                          : output_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie,
+                                                       kCandMaxTies, &s_ntie, sh.wave_cnt, o);
+  if (!ok) {
     __syncthreads();
     select_row(rv.p, n, k, o, sh);  // a boundary tie too long for the list
   }
@@ -311,7 +319,7 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
   dim3 fgrid((unsigned)((max_n + kCandSpan - 1) / kCandSpan), (unsigned)rows);
   topk_cand_filter_kernel<<<fgrid, 256, 0, st>>>(r, c.tau, c.cand, c.cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  constexpr size_t lds_max = (size_t)kCandCap * 8 + (size_t)(kCandMaxN / 32) * 4;
+  constexpr size_t lds_max = (size_t)kCandCap * 8 + (size_t)(kCandBitmapN / 32) * 4;
   static bool attr = false;
   if (!attr) {
     e = hipFuncSetAttribute((const void*)topk_cand_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -319,7 +327,9 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const size_t lds = (size_t)kCandCap * 8 + (size_t)((max_n + 31) / 32) * 4;
+  const int64_t bm = max_n > kCandBitmapN ? kCandBitmapN : max_n;
+  const size_t words = (size_t)((bm + 31) / 32) > (size_t)kCandSortBuf ? (size_t)((bm + 31) / 32) : kCandSortBuf;
+  const size_t lds = (size_t)kCandCap * 8 + words * 4;
   topk_cand_select_kernel<<<(unsigned)rows, kTopkThreads, lds, st>>>(r, k, c.tau, c.cand, c.cnt, idx_out,
                                                                      count_out);
   return hipGetLastError();

@@ -93,6 +93,12 @@ DECODE_64 = DecodeSpec("decode_B64_ctx16k_128k", 5, 64, 16384, 131072, 2048, 128
 
 WORKLOADS = {s.name: s for s in (TINY_F32, PREFILL_8K, PREFILL_32K, PREFILL_128K, DECODE_64)}
 
+# Million-token context (the write-up's closing outlook): the MLA-shaped
+# prefill at L = 2^20, run as chunks of queries over the growing key prefix,
+# and decode caches of up to 2^20 + a few entries.
+PREFILL_1M = PREFILL_128K.with_(name="prefill_L1048576_mla", wid=6, L=1 << 20)
+DECODE_1M = DecodeSpec("decode_B4_ctx1m", 7, 4, 65536, (1 << 20) + 64, 2048, 128, 576, 512)
+
 
 def _gen(device, wid: int, seed: int, tid: int) -> torch.Generator:
     g = torch.Generator(device=device)
@@ -140,15 +146,30 @@ def _index_rows(n: int, g, device, planted_every: int, fp8: bool):
 
 def make_prefill(spec: PrefillSpec, seed: int = 0, device="cpu") -> Dict[str, Optional[torch.Tensor]]:
     """Inputs of one causal prefill: queries and keys are the same L tokens."""
+    return make_prefill_chunk(spec, 0, seed, device)
+
+
+def make_prefill_chunk(spec: PrefillSpec, q_offset: int, seed: int = 0, device="cpu",
+                       queries: bool = True) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs of the last chunk of one causal prefill: keys for all L tokens,
+    index queries and attention queries only for tokens q_offset .. L-1 (the
+    whole prefill when q_offset = 0).  With queries=False only the key side
+    is drawn (q_idx, q_scale and q are None)."""
     dev = torch.device(device)
     L = spec.L
-    q_idx, q_scale = _index_rows(L, _gen(dev, spec.wid, seed, _T_QIDX), dev, 0, spec.fp8)
+    T = L - q_offset
+    if not 0 <= q_offset <= L:
+        raise ValueError("q_offset outside [0, L]")
+    q_idx = q_scale = q = None
+    if queries:
+        q_idx, q_scale = _index_rows(T, _gen(dev, spec.wid, seed, _T_QIDX), dev, 0, spec.fp8)
     k_idx, k_scale = _index_rows(L, _gen(dev, spec.wid, seed, _T_KIDX), dev, spec.planted_every, spec.fp8)
     wdt = torch.float32 if not spec.fp8 else torch.bfloat16
     w = _randn((IDX_DIM, IDX_DIM), _gen(dev, spec.wid, seed, _T_W), dev, 1.0 / math.sqrt(IDX_DIM), wdt)
     adt = torch.float32 if spec.attn_f32 else torch.bfloat16
     q_std = 1.0 if spec.qkv_unit else 1.0 / math.sqrt(spec.Dk)
-    q = _randn((L, spec.H, spec.Dk), _gen(dev, spec.wid, seed, _T_Q), dev, q_std, adt)
+    if queries:
+        q = _randn((T, spec.H, spec.Dk), _gen(dev, spec.wid, seed, _T_Q), dev, q_std, adt)
     if spec.shared_kv:
         kv = _randn((L, spec.Dk), _gen(dev, spec.wid, seed, _T_K), dev, q_std, adt)
         v = None

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
     for s in range(7):
         assert lib.dsa_status_str(s)
     assert lib.dsa_status_str(99) == b"unknown status"

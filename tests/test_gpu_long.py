@@ -1,0 +1,167 @@
+"""Long contexts on the GPU through the C ABI: a prefill run in chunks of
+queries (q_offset > 0) against the whole-sequence call and the oracle, a
+chunk of the 2^20-token prefill, and decode caches of up to 2^20 + 64
+entries.  Rules in tests/parity.py."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.dsa as od
+import parity as P
+from helpers import to_np
+from sparse_attention_long_indexer_amd import binding as B
+from sparse_attention_long_indexer_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    return torch.device("cuda:0")
+
+
+class RowsOf:
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, i):
+        return to_np(self.t[i])
+
+
+def forward(spec, x, dev, flags=0, q_offset=0):
+    T = x["q"].shape[0]
+    out = torch.empty((T, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
+    idx = torch.empty((T, spec.topk), dtype=torch.int32, device=dev)
+    B.dsa_forward(B.forward_args(x, spec.topk, spec.scale, spec.Dv, flags=flags, q_offset=q_offset), out,
+                  idx_out=idx)
+    torch.cuda.synchronize()
+    return out, idx
+
+
+def chunk_of(x, c0, c1):
+    """Queries c0..c1-1 over keys 0..c1-1 of whole-sequence inputs."""
+    y = dict(x)
+    for k in ("q_idx", "q_scale", "q"):
+        y[k] = x[k][c0:c1] if x[k] is not None else None
+    for k in ("k_idx", "k_scale", "kv", "v"):
+        y[k] = x[k][:c1] if x[k] is not None else None
+    return y
+
+
+def oracle_rows(spec, x, c0, o_c, i_c):
+    """Rows of a chunk whose attention ran through a split key loop (short
+    chunks combine partial softmax sums, so the bits differ from the
+    whole-sequence call): held to the oracle's attention bar instead."""
+    orc = od.PrefillOracle(to_np(x["q_idx"]), to_np(x["q_scale"]), to_np(x["k_idx"]), to_np(x["k_scale"]),
+                           to_np(x["w"]), RowsOf(x["q"]), to_np(x["kv"]), to_np(x["v"]), spec.topk, spec.scale,
+                           spec.Dv)
+    gi = i_c.cpu().numpy()
+    worst = 0.0
+    for r in range(o_c.shape[0]):
+        m = int((gi[r] >= 0).sum())
+        o, _ = orc.attend_row(c0 + r, gi[r][:m])
+        worst = max(worst, P.check_attn(od.as_f64(to_np(o_c[r])), o))
+    say(f"split rows {c0}..{c0 + o_c.shape[0]}: worst attention error / rms {worst:.3g}")
+
+
+CHUNKS = [(0, 1000), (1000, 1100), (1100, 1101), (1101, 6000)]
+
+
+@pytest.mark.parametrize("flags", [B.DSA_FLAG_FUSED, B.DSA_FLAG_MATERIALIZE], ids=["fused", "materialized"])
+def test_chunked_prefill_equals_whole(dev, flags):
+    spec = gen.PREFILL_8K.with_(L=6000, topk=1024)
+    say("chunked prefill", spec.L, flags)
+    x = gen.make_prefill(spec, seed=21, device=dev)
+    o_w, i_w = forward(spec, x, dev, flags)
+    for c0, c1 in CHUNKS:
+        o_c, i_c = forward(spec, chunk_of(x, c0, c1), dev, flags, q_offset=c0)
+        bad = (i_c != i_w[c0:c1]).any(dim=1).nonzero().flatten()
+        assert bad.numel() == 0, (c0, c1, (bad + c0)[:8].tolist())
+        if c1 - c0 >= 256:
+            assert torch.equal(o_c.view(torch.int16), o_w[c0:c1].view(torch.int16)), (c0, c1)
+        else:
+            say(f"max |chunk - whole| {float((o_c.float() - o_w[c0:c1].float()).abs().max()):.3g}")
+            oracle_rows(spec, x, c0, o_c, i_c)
+
+
+def test_chunked_prefill_128k(dev):
+    spec = gen.PREFILL_128K
+    say("chunked prefill", spec.L)
+    x = gen.make_prefill(spec, seed=22, device=dev)
+    o_w, i_w = forward(spec, x, dev)
+    half = spec.L // 2
+    for c0, c1 in ((0, half), (half, spec.L)):
+        o_c, i_c = forward(spec, chunk_of(x, c0, c1), dev, q_offset=c0)
+        assert torch.equal(i_c, i_w[c0:c1]), (c0, c1)
+        assert torch.equal(o_c.view(torch.int16), o_w[c0:c1].view(torch.int16)), (c0, c1)
+        del o_c, i_c
+
+
+def test_prefill_chunk_1m(dev):
+    """The last 1000 queries of the 2^20-token prefill: the fused path (rows
+    far longer than the select's bitmap, sorted output) equals the
+    materialised scores + radix select, and sampled rows match the oracle."""
+    spec = gen.PREFILL_1M
+    T = 1000
+    q0 = spec.L - T
+    say("prefill chunk", spec.L, "q_offset", q0)
+    x = gen.make_prefill_chunk(spec, q0, seed=23, device=dev)
+    o_f, i_f = forward(spec, x, dev, q_offset=q0)
+    o_m, i_m = forward(spec, x, dev, B.DSA_FLAG_MATERIALIZE, q_offset=q0)
+    bad = (i_f != i_m).any(dim=1).nonzero().flatten()
+    assert bad.numel() == 0, bad[:8].tolist()
+    assert torch.equal(o_f.view(torch.int16), o_m.view(torch.int16))
+    n = {k: to_np(v) for k, v in x.items() if k not in ("q",)}
+    orc = od.PrefillOracle(n["q_idx"], n["q_scale"], n["k_idx"], n["k_scale"], n["w"], RowsOf(x["q"]), n["kv"], None,
+                           spec.topk, spec.scale, spec.Dv, q_offset=q0)
+    gi = i_f.cpu().numpy()
+    diffs = 0
+    for t in (0, 1, 499, T - 2, T - 1):
+        sc = orc.scores_row(t)
+        sel = od.topk_row(sc, spec.topk)
+        d = P.check_topk_row(gi[t], sc, sel, spec.topk)
+        diffs += d
+        if d == 0:
+            o, _ = orc.attend_row(t, sel)
+            P.check_attn(od.as_f64(to_np(o_f[t])), o)
+    say("window diffs", diffs)
+    assert diffs <= 1
+
+
+def test_decode_1m(dev):
+    spec = gen.DECODE_1M
+    lengths = torch.tensor([(1 << 20) + 64, 600_000, 524_289, 70_000], dtype=torch.int64)
+    say("decode", spec.name, lengths.tolist())
+    x = gen.make_decode(spec, seed=24, device=dev, lengths=lengths)
+    out = torch.empty((spec.B, spec.H, spec.Dv), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((spec.B, spec.topk), dtype=torch.int32, device=dev)
+    args = B.forward_args(x, spec.topk, spec.scale, spec.Dv, mode=B.DSA_MODE_DECODE, max_len=int(lengths.max()))
+    B.dsa_forward(args, out, idx_out=idx)
+    torch.cuda.synchronize()
+    n = {k: to_np(v) for k, v in x.items() if k not in ("q", "kv", "lengths")}
+    dec = od.DecodeOracle(n["q_idx"], n["q_scale"], n["k_idx"], n["k_scale"], n["w"], RowsOf(x["q"]),
+                          RowsOf(x["kv"]), None, n["offsets"], spec.topk, spec.scale, spec.Dv)
+    gi = idx.cpu().numpy()
+    diffs = 0
+    for b in range(spec.B):
+        sc = dec.scores_seq(b)
+        sel = od.topk_row(sc, spec.topk)
+        d = P.check_topk_row(gi[b], sc, sel, spec.topk)
+        diffs += d
+        if d == 0:
+            _, o, _ = dec.seq(b)
+            P.check_attn(od.as_f64(to_np(out[b])), o)
+    say("decode window diffs", diffs)
+    # differing keys lie inside the boundary window (checked above); longer
+    # rows hold more keys within the window's fp32-vs-fp64 margin
+    assert diffs <= 2 * spec.B
