@@ -8,6 +8,10 @@ HBM.  The headline is the 131072-token causal prefill with k = 2048 and
 MLA-shaped attention (128 heads, key 576, value 512); the 64-sequence batched
 decode step is timed after it.  Prints one JSON line.
 
+--workload prefill_L1048576_mla times the 2^20-token prefill instead, as
+chunks of --chunk queries over the growing key prefix (a step is all the
+chunks), and a 64-sequence decode over caches of 2^19 .. 2^20 keys.
+
 The dominant kernel's duration is measured live with HIP events on the stream
 the kernel runs on; its roofline uses algorithmic FLOPs (or bytes) only.  The
 CPU baseline times the fp64 oracle on a bounded random sample of query rows of
@@ -144,6 +148,127 @@ def profile_attention(spec, x, reps):
     log(f"profiled: 1 copy of {n} bytes, {reps} attention launches")
 
 
+def decode_step_stats(B, gen, torch, dev, ds, lengths=None, reps=20):
+    """Time whole decode steps (fold, scores, top-k, attention) with HIP
+    events on the stream the library launches on."""
+    xd = gen.make_decode(ds, seed=0, device=dev, lengths=lengths)
+    dout = torch.empty((ds.B, ds.H, ds.Dv), dtype=torch.bfloat16, device=dev)
+    didx = torch.empty((ds.B, ds.topk), dtype=torch.int32, device=dev)
+    da = B.forward_args(xd, ds.topk, ds.scale, ds.Dv, mode=B.DSA_MODE_DECODE, max_len=int(xd["lengths"].max()))
+    dws = torch.empty(max(B.dsa_forward_workspace_size(da), 256), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        B.dsa_forward(da, dout, idx_out=didx, ws=dws)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(st)
+    for _ in range(reps):
+        B.dsa_forward(da, dout, idx_out=didx, ws=dws)
+    ev1.record(st)
+    torch.cuda.synchronize()
+    dms = ev0.elapsed_time(ev1) / reps
+    n = xd["lengths"]
+    byts = float(n.sum()) * 132 + float(torch.clamp(n, max=ds.topk).sum()) * ds.Dk * 2 \
+        + ds.B * ds.H * (ds.Dk + ds.Dv) * 2 + 2 * ds.B * ds.topk * 4
+    del xd, dout, didx, dws
+    return {"workload": ds.name, "queries_per_s": round(ds.B / (dms * 1e-3), 1),
+            "ms_per_step": round(dms, 4), "keys": int(n.sum()), "algorithmic_bytes": byts,
+            "roofline": {"bound": "hbm", "achieved": round(byts / (dms * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(byts / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                         "note": "warm caches; whole decode step"}}
+
+
+def bench_long(args, B, gen, torch, dev):
+    """The 2^20-token prefill as chunks of C queries (each chunk attends over
+    the keys of every earlier chunk and its own), then a 64-sequence decode
+    step over caches of 2^19 .. 2^20 keys.  All queries, keys and the latent
+    KV of the whole sequence are resident; one output buffer of C rows is
+    rewritten by every chunk (the 2^20-row output and the queries do not fit
+    in HBM together)."""
+    spec = gen.PREFILL_1M
+    L, k, C = spec.L, spec.topk, args.chunk
+    if L % C:
+        raise SystemExit("--chunk must divide 2^20")
+    log("workload", spec.name, f"generating inputs (chunks of {C})")
+    x = gen.make_prefill_chunk(spec, 0, seed=0, device=dev)
+    out = torch.empty((C, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
+    idx = torch.empty((L // C, C, k), dtype=torch.int32, device=dev)
+    fas = []
+    for c in range(L // C):
+        y = dict(x)
+        for key in ("q_idx", "q_scale", "q"):
+            y[key] = x[key][c * C:(c + 1) * C]
+        for key in ("k_idx", "k_scale", "kv"):
+            y[key] = x[key][:(c + 1) * C]
+        fas.append(B.forward_args(y, k, spec.scale, spec.Dv, q_offset=c * C))
+    ws = torch.empty(max(B.dsa_forward_workspace_size(fa) for fa in fas), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for c, fa in enumerate(fas):
+            B.dsa_forward(fa, out, idx_out=idx[c], ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    log(f"prefill {dt * 1e3:.1f} ms/step, {L / dt:.4g} tokens/s")
+
+    st = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fas) + 1)]
+    evs[0].record(st)
+    for c, fa in enumerate(fas):
+        B.dsa_forward(fa, out, idx_out=idx[c], ws=ws)
+        evs[c + 1].record(st)
+    torch.cuda.synchronize()
+    chunk_ms = [round(evs[c].elapsed_time(evs[c + 1]), 2) for c in range(len(fas))]
+    # attention of the last chunk alone: C queries over the whole 2^20 keys
+    qc = x["q"][L - C:]
+    B.dsa_sparse_attn(qc, x["kv"], idx[-1], spec.scale, Dv=spec.Dv, out=out)
+    reps = 3
+    evs[0].record(st)
+    for _ in range(reps):
+        B.dsa_sparse_attn(qc, x["kv"], idx[-1], spec.scale, Dv=spec.Dv, out=out)
+    evs[1].record(st)
+    torch.cuda.synchronize()
+    attn_ms = evs[0].elapsed_time(evs[1]) / reps
+    flops = 2.0 * spec.H * (spec.Dk + spec.Dv) * C * k
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    log(f"chunks {chunk_ms} ms; last-chunk attention {attn_ms:.2f} ms = {achieved:.1f} TFLOP/s")
+    result = {
+        "metric": "DSA prefill tokens/s at L=1M (query chunks over the growing key prefix), k=2048",
+        "value": round(L / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "dtype_detail": "indexer e4m3 x e4m3 -> fp32 MFMA; attention bf16 -> fp32 MFMA",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "L": L, "chunk": C, "topk": k, "heads": spec.H, "dk": spec.Dk,
+                   "dv": spec.Dv, "batch": 1, "index_dim": 128},
+        "chunk_ms": chunk_ms,
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<576,512,8>", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "ms_per_launch": round(attn_ms, 3), "algorithmic_flops_per_launch": flops,
+                     "note": "last chunk: the chunk's queries over all 2^20 keys"},
+    }
+    del out, ws
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(spec, x, budget_s=args.cpu_seconds)
+    del x, idx, fas
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        ds = gen.DECODE_64.with_(name="decode_B64_ctx512k_1m", wid=8, n_min=1 << 19, n_max=1 << 20)
+        log("decode: generating inputs")
+        result["decode"] = decode_step_stats(B, gen, torch, dev, ds)
+        log(f"decode {result['decode']['ms_per_step']:.3f} ms/step")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +278,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="row-time budget of the CPU baseline")
+    ap.add_argument("--chunk", type=int, default=131072, help="queries per chunk of the 2^20-token prefill")
     ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
                     help="only run the counter-profile sequence (a 2 GiB copy, then N attention launches)")
     args = ap.parse_args()
@@ -168,6 +294,9 @@ def main():
 
     B.lib()
     dev = torch.device("cuda:0")
+    if args.workload == gen.PREFILL_1M.name:
+        bench_long(args, B, gen, torch, dev)
+        return
     spec = gen.WORKLOADS[args.workload]
     log("workload", spec.name, "generating inputs")
     x = gen.make_prefill(spec, seed=0, device=dev)
@@ -238,35 +367,9 @@ def main():
     del out, idx, ws
 
     if not args.no_decode:
-        ds = gen.DECODE_64
         log("decode: generating inputs")
-        xd = gen.make_decode(ds, seed=0, device=dev)
-        dout = torch.empty((ds.B, ds.H, ds.Dv), dtype=torch.bfloat16, device=dev)
-        didx = torch.empty((ds.B, ds.topk), dtype=torch.int32, device=dev)
-        da = B.forward_args(xd, ds.topk, ds.scale, ds.Dv, mode=B.DSA_MODE_DECODE,
-                            max_len=int(xd["lengths"].max()))
-        dws = torch.empty(max(B.dsa_forward_workspace_size(da), 256), dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            B.dsa_forward(da, dout, idx_out=didx, ws=dws)
-        torch.cuda.synchronize()
-        reps = 20
-        ev0.record(st)
-        for _ in range(reps):
-            B.dsa_forward(da, dout, idx_out=didx, ws=dws)
-        ev1.record(st)
-        torch.cuda.synchronize()
-        dms = ev0.elapsed_time(ev1) / reps
-        n = xd["lengths"]
-        byts = float(n.sum()) * 132 + float(torch.clamp(n, max=ds.topk).sum()) * ds.Dk * 2 \
-            + ds.B * ds.H * (ds.Dk + ds.Dv) * 2 + 2 * ds.B * ds.topk * 4
-        result["decode"] = {"workload": ds.name, "queries_per_s": round(ds.B / (dms * 1e-3), 1),
-                            "ms_per_step": round(dms, 4), "algorithmic_bytes": byts,
-                            "roofline": {"bound": "hbm", "achieved": round(byts / (dms * 1e-3) / 1e9, 1),
-                                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                         "frac": round(byts / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                                         "note": "warm caches; whole decode step"}}
-        log(f"decode {dms:.3f} ms/step")
-        del xd, dout, didx, dws
+        result["decode"] = decode_step_stats(B, gen, torch, dev, gen.DECODE_64)
+        log(f"decode {result['decode']['ms_per_step']:.3f} ms/step")
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

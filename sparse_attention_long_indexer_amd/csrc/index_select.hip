@@ -8,6 +8,7 @@
 //     the score of rank r = ceil(1.75 * m * n_s / n) among the row's n_s
 //     samples (16-bit truncated, so tau never exceeds that sample's score).
 //     Expected survivors ~1.75 m.  Short rows (n <= kTakeAll) keep every key.
+//     Past 128K keys a refinement pass rescores one key in 32 around tau.
 //  2. filter: one FP8 MFMA pass over every causal (query, key) pair with
 //     keys in the A operand and queries in the B operand, so a lane owns one
 //     query and four keys; a score v = acc * ks survives if v >= tau_t / qs_t
@@ -18,7 +19,7 @@
 //     the segments.
 //  3. select: per row, u = v * qs and ReLU for each survivor, an exact radix
 //     select of the m best (score desc, index asc), and ascending output via
-//     a bitmap over key positions.  The survivors provably contain the exact
+//     a bitmap over key positions (position buckets for rows past 256K).  The survivors provably contain the exact
 //     answer when at least m of them reach tau; a row that fails this (or
 //     overflowed a segment) is queued for
 //  4. fallback: recompute that row's scores with the same MFMA and select
@@ -37,7 +38,7 @@ constexpr int kCap = 1536;                 // survivors per segment
 constexpr int kTakeAll = 5632;             // rows this short keep every key
 constexpr int kSampleMax = 4096;           // samples per row (max)
 constexpr float kAlpha = 1.75f;            // survivor target / m
-constexpr int64_t kSelBitmapN = 262144;    // longer rows emit their indices by sorting, not via a bitmap
+constexpr int64_t kSelBitmapN = 262144;    // longer rows emit their indices through buckets, not a bitmap
 
 __host__ __device__ inline int sample_stride(int64_t S) {
   int p = 32;
@@ -185,6 +186,110 @@ __global__ __launch_bounds__(kEstWaves * 64) void idx_estimate_kernel(const uint
     // positive ones (tau = the smallest positive float)
     const float tv = __uint_as_float(prefix << 16);
     if (lane == 0) tau[t] = tv > 0.f ? tv : 1.17549435e-38f;
+  }
+}
+
+// ---- 1b. threshold refinement for rows past 4096 * 32 keys ----------------
+// There the estimate's stride P grows while its sample stays at 4096 keys,
+// so the rank r shrinks (r ~ 14 at 2^20 keys) and tau scatters: too few
+// survivors send the row to the fallback.  This pass rescores one key in
+// every 32, counts per row the scores in [tau/2, 2 tau) on 128 bins evenly
+// spaced in the float bit pattern (1/64 of an octave each), and moves tau to
+// the lower edge of the bin where the count from the top reaches
+// r = ceil(1.75 m n_s / n) of the row's n_s samples.  A row whose r-th
+// sample lies below tau/2 gets tau/2.
+constexpr int kRefRows = 64;    // rows per block, 16 per wave
+constexpr int kRefKeys = 64;    // sampled keys per LDS tile
+constexpr int kRefBins = 128;
+constexpr int kRefStride = 32;
+constexpr int kRefBinShift = 17;  // 2 octaves = 2^24 bit steps over 128 bins
+
+__global__ __launch_bounds__(256) void idx_refine_kernel(const uint8_t* __restrict__ qf, const float* __restrict__ qs,
+                                                         const uint8_t* __restrict__ k8, const float* __restrict__ ks,
+                                                         int64_t T, int64_t S, int64_t topk, float* __restrict__ tau) {
+  __shared__ __align__(16) uint8_t ktile[2][kRefKeys * kIdxDim];
+  __shared__ __align__(16) float kst[2][kRefKeys];
+  __shared__ uint32_t hist[kRefRows][kRefBins];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t R0 = (int64_t)blockIdx.x * kRefRows;
+  const int64_t p0 = S - T;
+  // the lane's query row (B operand column c of wave w)
+  const int64_t t = R0 + 16 * w + c;
+  const int64_t tt = t < T ? t : T - 1;
+  const v8i bq = *(const v8i*)(qf + tt * kIdxDim + 32 * g);
+  const float qsc = qs[tt];
+  const int64_t n = min(p0 + tt + 1, S);
+  const float t1 = tau[tt];
+  const bool act = t < T && n > kTakeAll && t1 > 1.17549435e-38f && t1 < INFINITY;
+  const float lo = act ? 0.5f * t1 : INFINITY;
+  const uint32_t lob = __float_as_uint(lo);
+  const int64_t ns = act ? samples_upto(n - 1, kRefStride) : 0;  // sample j is the row's iff j < ns
+  const int64_t nsb = samples_upto(min(p0 + min(R0 + kRefRows - 1, T - 1), S - 1), kRefStride);
+
+  for (int i = threadIdx.x; i < kRefRows * kRefBins; i += 256) (&hist[0][0])[i] = 0u;
+
+  // 64 sampled keys x 128 B = 512 chunks (2 per thread) + 64 scales
+  auto issue = [&](int it, int buf) {
+    const int64_t j0 = (int64_t)it * kRefKeys;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int chunk = (i * 4 + w) * 64 + lane;
+      const int64_t js = j0 + (chunk >> 3);
+      const int64_t key = min(js * kRefStride + sample_off(js, kRefStride), S - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(k8 + key * kIdxDim + (chunk & 7) * 16),
+          (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint8_t*)ktile[buf] +
+                                                    (i * 4 + w) * 1024),
+          16, 0, 0);
+    }
+    if (w == 0) {
+      const int64_t js = j0 + lane;
+      const int64_t key = min(js * kRefStride + sample_off(js, kRefStride), S - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(ks + key),
+          (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)kst[buf]), 4, 0, 0);
+    }
+  };
+  const int ntiles = (int)((nsb + kRefKeys - 1) / kRefKeys);
+  if (ntiles > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) issue(it + 1, buf ^ 1);
+    const int64_t j0 = (int64_t)it * kRefKeys;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const v8i a = *(const v8i*)(ktile[buf] + (16 * kt + c) * kIdxDim + 32 * g);
+      const v4f acc = mfma_fp8_16x16x128(a, bq, (v4f){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jl = 16 * kt + 4 * g + i;   // C row 4g+i holds sample j0 + jl
+        const float u = (acc[i] * kst[buf][jl]) * qsc;
+        if (j0 + jl < ns && u >= lo) {
+          const uint32_t b = min((__float_as_uint(u) - lob) >> kRefBinShift, (uint32_t)(kRefBins - 1));
+          atomicAdd(&hist[16 * w + c][b], 1u);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (g == 0 && act) {
+    const int64_t m = min(topk, n);
+    int64_t r = (int64_t)ceilf(kAlpha * (float)m * (float)ns / (float)n);
+    r = r < 1 ? 1 : (r > ns ? ns : r);
+    uint32_t cum = 0;
+    float tv = lo;
+    for (int b = kRefBins - 1; b >= 0; --b) {
+      cum += hist[16 * w + c][b];
+      if (cum >= (uint32_t)r) {
+        tv = __uint_as_float(lob + ((uint32_t)b << kRefBinShift));
+        break;
+      }
+    }
+    tau[t] = tv;
   }
 }
 
@@ -395,13 +500,13 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
     int32_t* __restrict__ fb, int force_fallback) {
   extern __shared__ __align__(16) uint32_t sm[];
   uint2* cl = (uint2*)sm;                       // [kSelMax] (score key, position) pairs
-  uint32_t* sel = sm + 2 * kSelMax;             // [nwords] bitmap of kept positions (or a long row's sort buffer)
+  uint32_t* sel = sm + 2 * kSelMax;             // [nwords] bitmap of kept positions (or a long row's buckets)
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t wave_cnt[kSelWaves];
   __shared__ uint32_t s_sel[2];
   __shared__ int s_cnt[kSets * kSeg], s_cbase[kSets * kSeg + 1];
   __shared__ int32_t s_tie[kMaxTies];
-  __shared__ int s_ntie, s_bad, s_nbuf;
+  __shared__ int s_ntie, s_bad;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t = blockIdx.x;
   const int64_t n = min(S - T + t + 1, S);
@@ -413,13 +518,10 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   }
   const float qsc = qs[t];
   const float tt = tau[t];
-  const bool sorted = n > kSelBitmapN;
-  const int nwords = sorted ? 0 : (int)((n + 31) >> 5);
+  const bool bucketed = n > kSelBitmapN;
+  const int nwords = bucketed ? 0 : (int)((n + 31) >> 5);
   if (tid < kSets * kSeg) s_cnt[tid] = cnt_in[t * kSets * kSeg + tid];
-  if (tid == 0) {
-    s_ntie = 0;
-    s_nbuf = 0;
-  }
+  if (tid == 0) s_ntie = 0;
   for (int i = tid; i < nwords; i += kSelThreads) sel[i] = 0;
   __syncthreads();
   // chunk layout: segment gq owns chunks [s_cbase[gq], s_cbase[gq+1])
@@ -512,9 +614,8 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
                             s_sel, thr, need);
   // keys above the m-th best go to the bitmap, ties to a list; a
   // pathological tie at the boundary is settled exactly elsewhere
-  const bool ok = sorted ? output_sorted_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk,
-                                                                      (int32_t*)sel, &s_nbuf, s_tie, kMaxTies,
-                                                                      &s_ntie, o)
+  const bool ok = bucketed ? output_bucketed_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel,
+                                                                        s_tie, kMaxTies, &s_ntie, wave_cnt, o)
                           : output_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel, nwords,
                                                                 s_tie, kMaxTies, &s_ntie, wave_cnt, o);
   if (!ok) {
@@ -590,11 +691,15 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
   if (e != hipSuccess) return e;
   idx_estimate_kernel<<<(unsigned)((T + 15) / 16), kEstWaves * 64, 0, st>>>(qf, qs, k8, ks, T, S, topk, tau);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (sample_stride(S) > kRefStride) {
+    idx_refine_kernel<<<(unsigned)((T + kRefRows - 1) / kRefRows), 256, 0, st>>>(qf, qs, k8, ks, T, S, topk, tau);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   idx_filter_kernel<<<(unsigned)filter_items(T, S), 256, 0, st>>>(qf, qs, k8, ks, T, S, tau, cand, cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // bitmap words of the longest row with a bitmap, or the sort buffer
+  // bitmap words of the longest row with a bitmap, or the bucket pass's words
   const int64_t bn = S < kSelBitmapN ? S : kSelBitmapN;
-  const int64_t words = (bn + 31) / 32 > DSA_MAX_TOPK ? (bn + 31) / 32 : DSA_MAX_TOPK;
+  const int64_t words = S > kSelBitmapN && 2 * kOutBuckets > (bn + 31) / 32 ? 2 * kOutBuckets : (bn + 31) / 32;
   const size_t lds = (size_t)2 * kSelMax * 4 + (size_t)words * 4;
   static bool attr = false;
   if (!attr) {

@@ -240,25 +240,38 @@ __device__ inline bool output_from_candidates(const uint2* cl, int nslots, uint3
   return true;
 }
 
-// The same output without a bitmap, for rows too long for one in LDS: the m
+// The same output without a bitmap, for rows too long for one in LDS.  The
 // kept positions (keys above thr, then the `need` lowest-position keys equal
-// to thr) are gathered into buf (LDS, at least the next power of two >= m
-// entries) and sorted ascending with a block-wide bitonic sort.  *s_nbuf and
-// *s_ntie must be zeroed by the caller before a barrier.  Returns false, with
-// nothing written to o, when the tie list overflows.
+// to thr) are counted per bucket of 2^shift consecutive positions (4096
+// buckets span the row), an exclusive scan gives every bucket its output
+// range, each kept position is dropped into its bucket's range, and its
+// final place is the bucket start plus the number of smaller positions in
+// the same bucket (a bucket holds a handful of kept keys).
+// work: LDS, 2 * kOutBuckets words; m <= kOutBuckets.  *s_ntie must be
+// zeroed by the caller before a barrier.  Returns false, with nothing
+// written to o, when the tie list overflows.
+constexpr int kOutBuckets = 4096;
+
 template <int NT>
-__device__ inline bool output_sorted_from_candidates(const uint2* cl, int nslots, uint32_t thr, uint32_t need,
-                                                     int64_t n, int64_t m, int64_t topk, int32_t* buf,
-                                                     int* s_nbuf, int32_t* tie, int max_ties, int* s_ntie,
-                                                     int32_t* __restrict__ o) {
-  const int tid = threadIdx.x;
+__device__ inline bool output_bucketed_from_candidates(const uint2* cl, int nslots, uint32_t thr, uint32_t need,
+                                                       int64_t n, int64_t m, int64_t topk, uint32_t* work,
+                                                       int32_t* tie, int max_ties, int* s_ntie, uint32_t* wave_cnt,
+                                                       int32_t* __restrict__ o) {
+  constexpr int NW = NT / 64, PER = kOutBuckets / NT;
+  static_assert(PER * NT == kOutBuckets, "threads must divide the bucket count");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t* start = work;                        // [kOutBuckets] counts, then ranges
+  int32_t* buf = (int32_t*)(work + kOutBuckets);  // [m] kept positions by bucket
+  const int bits = 64 - __builtin_clzll((uint64_t)(n - 1) | 1ull);
+  const int shift = bits > 12 ? bits - 12 : 0;
+  for (int i = tid; i < kOutBuckets; i += NT) start[i] = 0u;
+  __syncthreads();
   for (int e = tid; e < nslots; e += NT) {
     const uint2 cv = cl[e];
-    const uint32_t key = cv.x;
     const int32_t p = (int32_t)cv.y;
-    if (key < thr || p < 0 || p >= n) continue;
-    if (key > thr) {
-      buf[atomicAdd(s_nbuf, 1)] = p;
+    if (cv.x < thr || p < 0 || p >= n) continue;
+    if (cv.x > thr) {
+      atomicAdd(&start[p >> shift], 1u);
     } else {
       const int q = atomicAdd(s_ntie, 1);
       if (q < max_ties) tie[q] = p;
@@ -267,35 +280,61 @@ __device__ inline bool output_sorted_from_candidates(const uint2* cl, int nslots
   __syncthreads();
   const int ntie = *s_ntie;
   if (ntie > max_ties) return false;
-  for (int i = tid; i < ntie; i += NT) {
+  auto tie_kept = [&](int i) {
     const int32_t p = tie[i];
     int rank = 0;
     for (int j = 0; j < ntie; ++j) rank += tie[j] < p ? 1 : 0;
-    if (rank < (int)need) buf[atomicAdd(s_nbuf, 1)] = p;
+    return rank < (int)need;
+  };
+  for (int i = tid; i < ntie; i += NT)
+    if (tie_kept(i)) atomicAdd(&start[tie[i] >> shift], 1u);
+  __syncthreads();
+  // exclusive scan of the bucket counts; thread tid owns PER buckets
+  uint32_t v[PER], mine = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    v[j] = start[tid * PER + j];
+    mine += v[j];
+  }
+  uint32_t incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) wave_cnt[w] = incl;
+  __syncthreads();
+  uint32_t run = incl - mine;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) run += (i < w) ? wave_cnt[i] : 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    start[tid * PER + j] = run;
+    run += v[j];
   }
   __syncthreads();
-  const int cnt = *s_nbuf;  // == m
-  int len = 1;
-  while (len < cnt) len <<= 1;
-  for (int i = cnt + tid; i < len; i += NT) buf[i] = 0x7FFFFFFF;
-  __syncthreads();
-  for (int k = 2; k <= len; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < len; i += NT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t x = buf[i], y = buf[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            buf[i] = y;
-            buf[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
+  // drop each kept position into its bucket (start[b] ends as bucket b's end)
+  for (int e = tid; e < nslots; e += NT) {
+    const uint2 cv = cl[e];
+    const int32_t p = (int32_t)cv.y;
+    if (cv.x <= thr || p < 0 || p >= n) continue;
+    const uint32_t slot = atomicAdd(&start[p >> shift], 1u);
+    if (slot < (uint32_t)kOutBuckets) buf[slot] = p;
   }
-  for (int64_t i = tid; i < topk; i += NT) o[i] = i < m ? buf[i] : -1;
+  for (int i = tid; i < ntie; i += NT) {
+    if (!tie_kept(i)) continue;
+    const uint32_t slot = atomicAdd(&start[tie[i] >> shift], 1u);
+    if (slot < (uint32_t)kOutBuckets) buf[slot] = tie[i];
+  }
+  __syncthreads();
+  for (int i = tid; i < (int)m; i += NT) {
+    const int32_t p = buf[i];
+    const int b = p >> shift;
+    const uint32_t lo = b ? start[b - 1] : 0u, hi = start[b];
+    uint32_t rank = 0;
+    for (uint32_t j = lo; j < hi; ++j) rank += buf[j] < p ? 1u : 0u;
+    o[lo + rank] = p;
+  }
+  for (int64_t i = m + tid; i < topk; i += NT) o[i] = -1;
   return true;
 }
 

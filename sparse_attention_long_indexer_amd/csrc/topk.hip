@@ -60,15 +60,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(TopkRows R, in
 // ---- candidate path for few long rows --------------------------------------
 constexpr int kCandCap = 8192;          // candidates a row may stage in LDS
 constexpr int kCandWin = 64;            // sampled keys per window (one wave)
-constexpr int kCandWins = 64;           // windows per row, one per stratum
-constexpr int kCandSample = kCandWin * kCandWins;
+constexpr int kCandWins = 64;           // windows per row (at least), one per stratum
+constexpr int kCandWinsMax = 4096;      // ... and at most
 constexpr int kCandSpan = 4096;         // keys per filter block
 constexpr int kCandThreads = 512;
 constexpr int kCandWaves = kCandThreads / 64;
 constexpr int kCandMaxTies = 512;
 constexpr int64_t kCandMinN = 16384;    // shorter rows: one block per row is enough
 constexpr int64_t kCandBitmapN = 524288;  // rows up to this long: ascending output via an LDS bitmap
-constexpr int kCandSortBuf = kCandCap / 2;  // longer rows: the kept positions (m <= cap / 2) sorted in LDS
 constexpr int64_t kCandMaxRows = 512;   // more rows fill the chip one block per row
 
 static bool topk_use_candidates(int64_t rows, int64_t max_n, int64_t k) {
@@ -85,16 +84,17 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   return x;
 }
 
-// tau[row]: the r-th largest of 4096 sampled keys (one 64-key window at a
-// hashed offset inside each of 64 equal strata), r chosen so that about
-// min(1.75 m, (m + cap) / 2) keys of the row reach it.  0 (below every key)
-// when the whole row fits the candidate list.  A threshold on the zero
+// tau[row]: the r-th largest of a sample of the row's scores: one 64-key
+// window at a hashed offset inside each of nw equal strata, nw = n / 2048
+// clamped to [64, 4096] (one key in 32 up to 8M keys), r chosen so that
+// about min(1.75 m, (m + cap) / 2) keys of the row reach it.  0 (below every
+// key) when the whole row fits the candidate list.  A threshold on the zero
 // score is raised past it, so ReLU's zeros do not flood the list.  Also
 // clears the row's candidate count.
 __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRows R, int64_t k,
                                                                          uint32_t* __restrict__ tau,
                                                                          int32_t* __restrict__ cnt) {
-  __shared__ uint32_t skey[kCandSample];
+  __shared__ uint32_t wstart[kCandWinsMax];
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t scan[kCandWaves];
   __shared__ uint32_t s_out[2];
@@ -107,24 +107,24 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRo
     if (tid == 0) tau[row] = 0u;
     return;
   }
+  const int64_t nw64 = n / (32 * kCandWin);
+  const int nw = (int)(nw64 < kCandWins ? kCandWins : (nw64 > kCandWinsMax ? kCandWinsMax : nw64));
+  const int64_t nsamp = (int64_t)nw * kCandWin;
   const double target = fmin(1.75 * (double)m, 0.5 * (double)(m + kCandCap));
-  int64_t r = (int64_t)ceil(target * kCandSample / (double)n);
-  r = r < 1 ? 1 : (r > kCandSample ? kCandSample : r);
-  constexpr int WPW = kCandWins / kCandWaves;  // windows per wave
-  float v[WPW];
-#pragma unroll
-  for (int q = 0; q < WPW; ++q) {
-    const int wi = w + q * kCandWaves;
-    const int64_t s0 = n * wi / kCandWins, s1 = n * (wi + 1) / kCandWins;
-    const uint64_t slots = (uint64_t)(s1 - s0 - kCandWin + 1);  // n > cap, so >= 65
-    const int64_t start = s0 + (int64_t)(mix32((uint32_t)(row * kCandWins + wi) ^ 0x9e3779b9u) % slots);
-    v[q] = rv.p[start + lane];
+  int64_t r = (int64_t)ceil(target * (double)nsamp / (double)n);
+  r = r < 1 ? 1 : (r > nsamp ? nsamp : r);
+  // strata hold >= 128 keys (n > cap, nw <= max(64, n / 2048)), so every
+  // window fits inside its stratum
+  for (int wi = tid; wi < nw; wi += kCandThreads) {
+    const int64_t s0 = n * wi / nw, s1 = n * (wi + 1) / nw;
+    const uint64_t slots = (uint64_t)(s1 - s0 - kCandWin + 1);
+    wstart[wi] = (uint32_t)(s0 + (int64_t)(mix32((uint32_t)(row * kCandWinsMax + wi) ^ 0x9e3779b9u) % slots));
   }
+  __syncthreads();
+  auto key_at = [&](int64_t i) { return score_key(rv.p[wstart[i >> 6] + (i & (kCandWin - 1))]); };
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int q = 0; q < WPW; ++q) {
-    const uint32_t key = score_key(v[q]);
-    skey[(w + q * kCandWaves) * kCandWin + lane] = key;
+  for (int64_t i = tid; i < nsamp; i += kCandThreads) {
+    const uint32_t key = key_at(i);
     mn = min(mn, key);
     mx = max(mx, key);
   }
@@ -144,8 +144,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRo
   }
   __syncthreads();
   uint32_t thr, need;
-  radix_select<kCandThreads>([&](int64_t i) { return skey[i]; }, kCandSample, (uint32_t)r, mn, mx, hist, scan,
-                             s_out, thr, need);
+  radix_select<kCandThreads>(key_at, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr, need);
   if (tid == 0) tau[row] = thr == kZeroKey ? kZeroKey + 1 : thr;
 }
 
@@ -216,10 +215,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
   constexpr int NT = kTopkThreads;
   extern __shared__ __align__(16) uint32_t sm[];
   uint2* cl = (uint2*)sm;                  // [kCandCap] (key, position)
-  uint32_t* bitmap = sm + 2 * kCandCap;    // [nwords], or the sort buffer of a long row
+  uint32_t* bitmap = sm + 2 * kCandCap;    // [nwords], or a long row's position buckets
   __shared__ TopkShared sh;
   __shared__ int32_t s_tie[kCandMaxTies];
-  __shared__ int s_ntie, s_nbuf;
+  __shared__ int s_ntie;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t row = blockIdx.x;
   const RowView rv = topk_row_view(R, row);
@@ -236,13 +235,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
     select_row(rv.p, n, k, o, sh);
     return;
   }
-  const bool sorted = n > kCandBitmapN;
-  const int nwords = sorted ? 0 : (int)((n + 31) >> 5);
+  const bool bucketed = n > kCandBitmapN;
+  const int nwords = bucketed ? 0 : (int)((n + 31) >> 5);
   for (int i = tid; i < nwords; i += NT) bitmap[i] = 0u;
-  if (tid == 0) {
-    s_ntie = 0;
-    s_nbuf = 0;
-  }
+  if (tid == 0) s_ntie = 0;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   const uint2* cr = cand + row * kCandCap;
   for (int e = tid; e < c; e += NT) {
@@ -269,8 +265,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
   uint32_t thr, need;
   radix_select<NT>([&](int64_t e) { return cl[e].x; }, c, (uint32_t)m, tk != 0u ? tk : mn, mx, sh.hist,
                    sh.wave_cnt, sh.sel, thr, need);
-  const bool ok = sorted ? output_sorted_from_candidates<NT>(cl, c, thr, need, n, m, k, (int32_t*)bitmap, &s_nbuf,
-                                                             s_tie, kCandMaxTies, &s_ntie, o)
+  const bool ok = bucketed ? output_bucketed_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, s_tie, kCandMaxTies,
+                                                               &s_ntie, sh.wave_cnt, o)
                           : output_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie,
                                                        kCandMaxTies, &s_ntie, sh.wave_cnt, o);
   if (!ok) {
@@ -328,7 +324,9 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
     attr = true;
   }
   const int64_t bm = max_n > kCandBitmapN ? kCandBitmapN : max_n;
-  const size_t words = (size_t)((bm + 31) / 32) > (size_t)kCandSortBuf ? (size_t)((bm + 31) / 32) : kCandSortBuf;
+  const size_t words = max_n > kCandBitmapN && (size_t)(2 * kOutBuckets) > (size_t)((bm + 31) / 32)
+                           ? (size_t)(2 * kOutBuckets)
+                           : (size_t)((bm + 31) / 32);
   const size_t lds = (size_t)kCandCap * 8 + words * 4;
   topk_cand_select_kernel<<<(unsigned)rows, kTopkThreads, lds, st>>>(r, k, c.tau, c.cand, c.cnt, idx_out,
                                                                      count_out);
