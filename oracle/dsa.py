@@ -117,6 +117,22 @@ def topk_row(scores: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:m])
 
 
+def dynamic_k(scores: np.ndarray, k_max: int, k_min: int, theta: float) -> int:
+    """Per-query key budget for a dynamic k (reading R19 of the write-up's
+    outlook on k that adapts instead of a fixed top-k, section 6): the number
+    of keys whose index score exceeds theta, kept within [k_min, k_max] and
+    never above the row's n keys.  theta = -inf gives the fixed min(k_max, n)."""
+    n = np.asarray(scores).shape[0]
+    above = int(np.count_nonzero(np.asarray(scores, np.float64) > theta))
+    return min(n, k_max, max(k_min, above))
+
+
+def topk_row_dynamic(scores: np.ndarray, k_max: int, k_min: int, theta: float) -> np.ndarray:
+    """The dynamic_k(...) best keys of one row, under the same order and
+    output convention as topk_row."""
+    return topk_row(scores, dynamic_k(scores, k_max, k_min, theta))
+
+
 def pad_idx(sel: np.ndarray, k: int) -> np.ndarray:
     out = np.full(k, -1, dtype=np.int32)
     out[: sel.shape[0]] = sel

@@ -326,6 +326,32 @@ def pin_topk_properties(od, oc):
     assert list(padded) == [3, 7, -1, -1, -1]
 
 
+def pin_dynamic_k(od, oc):
+    """Dynamic k against brute force over every subset size, plus its limits:
+    theta = -inf is the fixed top-k, a theta above every score leaves k_min,
+    and between the two the set is exactly the keys above theta."""
+    rng = np.random.default_rng(17)
+    for n in (1, 3, 8, 40, 200):
+        for _ in range(6):
+            s = np.maximum(0.0, np.round(rng.standard_normal(n) * 4) / 4)   # ties, zeros
+            for k_max in (1, 5, 16, 64, 500):
+                for k_min in (0, 1, 3, k_max):
+                    if k_min > k_max:
+                        continue
+                    for theta in (-np.inf, 0.0, 0.25, 0.5, 1.0, 100.0):
+                        sel = od.topk_row_dynamic(s, k_max, k_min, theta)
+                        above = [i for i in range(n) if s[i] > theta]
+                        want = min(n, k_max, max(k_min, len(above)))
+                        assert sel.shape == (want,), (n, k_max, k_min, theta)
+                        # brute force: the want best under (score desc, index asc)
+                        order = sorted(range(n), key=lambda i: (-s[i], i))
+                        assert list(sel) == sorted(order[:want])
+                        if k_min <= len(above) <= k_max:
+                            assert list(sel) == above
+                    assert np.array_equal(od.topk_row_dynamic(s, k_max, k_min, -np.inf), od.topk_row(s, k_max))
+                    assert od.topk_row_dynamic(s, k_max, k_min, 1e9).shape == (min(n, k_min),)
+
+
 # --------------------------------------------------------------- attention --
 
 def pin_attend_special_cases(od, oc):
@@ -418,6 +444,6 @@ ALL_PINS = [
     pin_e4m3_decode_matches_library, pin_e4m3_landmarks, pin_e4m3_encode_matches_library,
     pin_e4m3_encode_midpoints_and_saturation, pin_bf16_decode_matches_library, pin_fold_orientation,
     pin_requant_closed_forms, pin_scores_one_hot, pin_brute_force, pin_prefill_chunk_brute_force,
-    pin_scores_causal_relu, pin_topk_properties,
+    pin_scores_causal_relu, pin_topk_properties, pin_dynamic_k,
     pin_attend_special_cases, pin_sparse_equals_dense, pin_decode_equals_prefill_row, pin_page_constants,
 ]

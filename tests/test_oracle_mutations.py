@@ -147,7 +147,19 @@ def _chunk_ignores_offset(self, t):
     return od.index_scores_row(self.q_vals[t], self.q_scale_of(t), self.k_vals, self.k_scale, t)
 
 
+def _dynamic_k_ge(scores, k_max, k_min, theta):
+    n = np.asarray(scores).shape[0]
+    return min(n, k_max, max(k_min, int(np.count_nonzero(np.asarray(scores) >= theta))))
+
+
+def _dynamic_k_no_floor(scores, k_max, k_min, theta):
+    n = np.asarray(scores).shape[0]
+    return min(n, k_max, int(np.count_nonzero(np.asarray(scores) > theta)))
+
+
 MUTATIONS = {
+    "dynamic_k_counts_ties_at_theta": (od, "dynamic_k", _dynamic_k_ge),
+    "dynamic_k_ignores_k_min": (od, "dynamic_k", _dynamic_k_no_floor),
     "prefill_chunk_ignores_offset": (od.PrefillOracle, "scores_row", _chunk_ignores_offset),
     "fold_transposed": (od, "fold", _fold_transposed),
     "requant_wrong_constant": (od, "requant", _requant_wrong_const),
