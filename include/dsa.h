@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 #define DSA_INDEX_DIM 128   /* index-key width, write-up section 2.2 */
 #define DSA_MAX_TOPK 4096
 
@@ -71,6 +71,8 @@ typedef enum {
                                      prefills (FP8 index only) */
 #define DSA_FLAG_FORCE_FALLBACK 4u /* fused path: settle every long row with
                                      the exact recompute fallback (testing) */
+#define DSA_FLAG_DYNAMIC_K 8u     /* per-query budget from dyn_theta and
+                                     dyn_k_min, as dsa_topk_dynamic */
 
 int dsa_abi_version(void);
 const char* dsa_status_str(dsa_status_t s);
@@ -139,6 +141,21 @@ dsa_status_t dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t S, con
                       void* stream);
 
 /*
+ * Top-k with a per-row budget (the write-up's outlook, section 6: a k that
+ * adapts per query instead of a fixed top-k).  Row t keeps
+ *   m_t = min(n_t, k_max, max(k_min, #{s < n_t : scores[t][s] > theta}))
+ * keys, the m_t best under dsa_topk's order, written as dsa_topk writes them
+ * (ascending, idx_out[t][m_t .. k_max) = -1); count_out[t] = m_t.
+ * theta = -inf is dsa_topk with k = k_max.  0 <= k_min <= k_max <=
+ * DSA_MAX_TOPK and theta not NaN, else DSA_ERR_SHAPE.  m_t may be 0 (k_min
+ * = 0 and no score above theta): the row is all -1.
+ * Workspace: dsa_topk_workspace_size(T, S, k_max) bytes.
+ */
+dsa_status_t dsa_topk_dynamic(const float* scores, int64_t ld, int64_t T, int64_t S, const int64_t* q_pos,
+                              int64_t k_max, int64_t k_min, float theta, int32_t* idx_out,
+                              int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Sparse MQA attention over the selected rows (write-up sections 2.3, 3.1).
  * For each query t and head h, over the valid entries s of idx[t] (entries
  * after the first -1 are ignored):
@@ -186,6 +203,8 @@ dsa_status_t dsa_sparse_attn(const void* q, int64_t T, int64_t H, int64_t Dk, ds
  *   idx_out [B][k] holds indices local to each sequence's cache.
  *   max_len is an upper bound on every n_b (host value, used to size work;
  *   BF16 attention needs max_len * ld * 2 <= 4 GiB, as for dsa_sparse_attn).
+ * With DSA_FLAG_DYNAMIC_K each query keeps m_t keys as dsa_topk_dynamic
+ * (k_max = topk) and attends over those; a query with m_t = 0 gets out = 0.
  * idx_out may be NULL (the indices then live only in the workspace).
  * Workspace: dsa_forward_workspace_size(args) bytes.
  */
@@ -213,6 +232,8 @@ typedef struct dsa_forward_args {
   int64_t topk;
   float scale;
   int64_t q_offset;           /* PREFILL: position of the first query */
+  float dyn_theta;            /* DSA_FLAG_DYNAMIC_K: score threshold theta */
+  int64_t dyn_k_min;          /* DSA_FLAG_DYNAMIC_K: k_min (k_max = topk) */
 } dsa_forward_args;
 
 size_t dsa_forward_workspace_size(const dsa_forward_args* a);

@@ -22,13 +22,14 @@ DSA_MODE_PREFILL, DSA_MODE_DECODE = 0, 1
 DSA_FLAG_MATERIALIZE = 1
 DSA_FLAG_FUSED = 2
 DSA_FLAG_FORCE_FALLBACK = 4
+DSA_FLAG_DYNAMIC_K = 8
 INDEX_DIM = 128
 MAX_TOPK = 4096
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTED = [
     "dsa_abi_version", "dsa_status_str", "dsa_fold_index_query", "dsa_index_scores",
-    "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
+    "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_dynamic", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
     "dsa_forward_workspace_size", "dsa_forward",
 ]
 
@@ -49,6 +50,7 @@ class ForwardArgs(ctypes.Structure):
         ("H", ctypes.c_int64), ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64), ("kv", ctypes.c_void_p),
         ("ld_kv", ctypes.c_int64), ("v", ctypes.c_void_p), ("ld_v", ctypes.c_int64),
         ("topk", ctypes.c_int64), ("scale", ctypes.c_float), ("q_offset", ctypes.c_int64),
+        ("dyn_theta", ctypes.c_float), ("dyn_k_min", ctypes.c_int64),
     ]
 
 
@@ -65,6 +67,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                              c_int),
         "dsa_topk_workspace_size": ([c_i64, c_i64, c_i64], c_sz),
         "dsa_topk": ([c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp], c_int),
+        "dsa_topk_dynamic": ([c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_i64, c_f, c_vp, c_vp, c_vp, c_sz, c_vp],
+                             c_int),
         "dsa_sparse_attn_workspace_size": ([c_i64, c_i64, c_i64, c_i64, c_int], c_sz),
         "dsa_sparse_attn": ([c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64,
                              c_f, c_vp, c_vp, c_vp, c_sz, c_vp], c_int),
@@ -158,6 +162,19 @@ def dsa_topk(scores, k, S=None, q_pos=None, idx_out=None, count_out=None, stream
     return idx_out
 
 
+def dsa_topk_dynamic(scores, k_max, k_min, theta, S=None, q_pos=None, idx_out=None, count_out=None, stream=None):
+    T, ld = scores.shape
+    S = ld if S is None else S
+    if idx_out is None:
+        idx_out = torch.empty((T, k_max), dtype=torch.int32, device=scores.device)
+    wsb = lib().dsa_topk_workspace_size(T, S, k_max)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=scores.device)
+    _check("dsa_topk_dynamic", lib().dsa_topk_dynamic(_p(scores), ld, T, S, _p(q_pos), k_max, k_min,
+                                                      ctypes.c_float(theta), _p(idx_out), _p(count_out), _p(ws),
+                                                      wsb, _stream(stream)))
+    return idx_out
+
+
 def dsa_sparse_attn(q, kv, idx, scale, v=None, Dv=None, out=None, lse_out=None, stream=None):
     T, H, Dk = q.shape
     S = kv.shape[0]
@@ -175,7 +192,7 @@ def dsa_sparse_attn(q, kv, idx, scale, v=None, Dv=None, out=None, lse_out=None, 
 
 
 def forward_args(x: dict, topk: int, scale: float, Dv: int, mode: int = DSA_MODE_PREFILL, flags: int = 0,
-                 max_len: int = 0, q_offset: int = 0):
+                 max_len: int = 0, q_offset: int = 0, dyn_theta: Optional[float] = None, dyn_k_min: int = 0):
     """Build the dsa_forward argument struct from an input dict of device
     tensors (keys as produced by the input generators).  For a prefill chunk
     (q_offset > 0) the query tensors hold the chunk's rows and the key
@@ -203,6 +220,10 @@ def forward_args(x: dict, topk: int, scale: float, Dv: int, mode: int = DSA_MODE
     a.topk = topk
     a.scale = scale
     a.q_offset = q_offset
+    if dyn_theta is not None:
+        a.flags |= DSA_FLAG_DYNAMIC_K
+        a.dyn_theta = dyn_theta
+        a.dyn_k_min = dyn_k_min
     if mode == DSA_MODE_DECODE:
         a.seq_offsets = x["offsets"].data_ptr()
         a.total_keys = x["k_idx"].shape[0]

@@ -155,6 +155,9 @@ dsa_status_t check_forward(const dsa_forward_args* a) {
   if (a->mode != DSA_MODE_PREFILL && a->mode != DSA_MODE_DECODE) return DSA_ERR_UNSUPPORTED;
   if (a->T < 0 || a->topk < 1 || a->topk > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
   if (a->q_offset < 0 || (a->mode == DSA_MODE_DECODE && a->q_offset != 0)) return DSA_ERR_SHAPE;
+  if ((a->flags & DSA_FLAG_DYNAMIC_K) &&
+      (a->dyn_k_min < 0 || a->dyn_k_min > a->topk || a->dyn_theta != a->dyn_theta))
+    return DSA_ERR_SHAPE;
   if (a->mode == DSA_MODE_PREFILL && a->q_offset > (int64_t(1) << 31) - 1 - a->T) return DSA_ERR_SHAPE;
   if (a->mode == DSA_MODE_DECODE) {
     if (a->idx_dtype != DSA_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
@@ -230,21 +233,29 @@ size_t dsa_topk_workspace_size(int64_t T, int64_t S, int64_t k) {
   return topk_workspace_bytes(T, S, k);
 }
 
-dsa_status_t dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t S, const int64_t* q_pos,
-                      int64_t k, int32_t* idx_out, int32_t* count_out, void* ws, size_t ws_bytes,
-                      void* stream) {
+dsa_status_t dsa_topk_dynamic(const float* scores, int64_t ld, int64_t T, int64_t S, const int64_t* q_pos,
+                              int64_t k_max, int64_t k_min, float theta, int32_t* idx_out, int32_t* count_out,
+                              void* ws, size_t ws_bytes, void* stream) {
   try {
-    if (T < 0 || S < 0 || ld < S || k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+    if (T < 0 || S < 0 || ld < S || k_max < 1 || k_max > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
+    if (k_min < 0 || k_min > k_max || theta != theta) return DSA_ERR_SHAPE;
     if (T == 0) return DSA_OK;
     if (!idx_out || (!scores && S > 0)) return DSA_ERR_NULL;
-    const size_t need = topk_workspace_bytes(T, S, k);
+    const size_t need = topk_workspace_bytes(T, S, k_max);
     if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
     DSA_TRY(check_device());
     TopkRows r{scores, ld, nullptr, q_pos, S, nullptr, 0, 0};
-    return from_hip(launch_topk(r, T, S, k, idx_out, count_out, ws, as_stream(stream)));
+    return from_hip(launch_topk(r, T, S, k_max, idx_out, count_out, ws, as_stream(stream), DynK{theta, k_min}));
   } catch (...) {
     return DSA_ERR_DEVICE;
   }
+}
+
+dsa_status_t dsa_topk(const float* scores, int64_t ld, int64_t T, int64_t S, const int64_t* q_pos,
+                      int64_t k, int32_t* idx_out, int32_t* count_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return dsa_topk_dynamic(scores, ld, T, S, q_pos, k, 0, -__builtin_huge_valf(), idx_out, count_out, ws, ws_bytes,
+                          stream);
 }
 
 size_t dsa_sparse_attn_workspace_size(int64_t T, int64_t H, int64_t Dv, int64_t k,
@@ -311,6 +322,7 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
     float* sc = (float*)(base + p.sc_off);
     const bool fp8 = a->idx_dtype == DSA_FP8_E4M3;
     const int64_t R = a->T;
+    const DynK dyn = (a->flags & DSA_FLAG_DYNAMIC_K) ? DynK{a->dyn_theta, a->dyn_k_min} : kFixedK;
 
     hipError_t e = launch_fold(a->q_idx, a->q_scale, fp8, a->w_index, a->w_dtype == DSA_BF16, R, qf,
                                qs, st);
@@ -335,7 +347,7 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
     if (p.fused) {
       const int64_t S = prefill_keys(a);
       e = launch_index_select((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale, R, S, a->topk, idx,
-                              sc, (a->flags & DSA_FLAG_FORCE_FALLBACK) != 0, st);
+                              sc, (a->flags & DSA_FLAG_FORCE_FALLBACK) != 0, st, dyn);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
       at.seq_offsets = nullptr;
       at.S = S;
@@ -347,7 +359,7 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
                                 st);
         if (e != hipSuccess) return DSA_ERR_DEVICE;
         TopkRows tr{sc, S, nullptr, nullptr, S, nullptr, r0, a->q_offset};
-        e = launch_topk(tr, r1 - r0, S, a->topk, idx + r0 * a->topk, nullptr, nullptr, st);
+        e = launch_topk(tr, r1 - r0, S, a->topk, idx + r0 * a->topk, nullptr, nullptr, st, dyn);
         if (e != hipSuccess) return DSA_ERR_DEVICE;
       }
       at.seq_offsets = nullptr;
@@ -357,7 +369,8 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
                                      a->seq_offsets, R, a->max_len, sc, st);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
       TopkRows tr{sc, 0, nullptr, nullptr, 0, a->seq_offsets, 0, 0};
-      e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, p.topk_bytes ? base + p.topk_off : nullptr, st);
+      e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, p.topk_bytes ? base + p.topk_off : nullptr, st,
+                      dyn);
       if (e != hipSuccess) return DSA_ERR_DEVICE;
       at.seq_offsets = a->seq_offsets;
       at.S = a->total_keys;

@@ -497,7 +497,7 @@ constexpr int kMaxTies = 512;             // keys equal to the m-th best kept in
 __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
     const float* __restrict__ qs, const float* __restrict__ tau, const uint2* __restrict__ cand,
     const int32_t* __restrict__ cnt_in, int64_t T, int64_t S, int64_t topk, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ fb, int force_fallback) {
+    int32_t* __restrict__ fb, int force_fallback, DynK dyn) {
   extern __shared__ __align__(16) uint32_t sm[];
   uint2* cl = (uint2*)sm;                       // [kSelMax] (score key, position) pairs
   uint32_t* sel = sm + 2 * kSelMax;             // [nwords] bitmap of kept positions (or a long row's buckets)
@@ -510,9 +510,9 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t t = blockIdx.x;
   const int64_t n = min(S - T + t + 1, S);
-  const int64_t m = min(topk, n);
+  int64_t m = min(topk, n);
   int32_t* o = idx_out + t * topk;
-  if (n <= topk) {
+  if (n <= topk && !dyn_on(dyn)) {  // (a dynamic k scores short rows too: they keep every key as a survivor)
     for (int64_t i = tid; i < topk; i += kSelThreads) o[i] = i < n ? (int32_t)i : -1;
     return;
   }
@@ -609,9 +609,24 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   // the m-th best key lies in [key(tau), max] (or [min, max] when every key
   // was kept)
   const uint32_t lo = tt != -INFINITY ? score_key(tt) : mn;
-  uint32_t thr, need;
-  radix_select<kSelThreads>([&](int64_t e) { return cl[e].x; }, nslots, (uint32_t)m, lo, mx, hist, wave_cnt,
-                            s_sel, thr, need);
+  auto key_at = [&](int64_t e) { return cl[e].x; };
+  uint32_t thr = lo, need = 0;
+  if (n > topk) radix_select<kSelThreads>(key_at, nslots, (uint32_t)m, lo, mx, hist, wave_cnt, s_sel, thr, need);
+  // dynamic k: once the m-th best is at or below theta, every key above
+  // theta is a survivor (the m-th best is >= tau)
+  const int64_t mm = dyn_budget<kSelThreads>(key_at, nslots, m, thr, dyn, wave_cnt);
+  if (n <= topk && mm == m) {
+    for (int64_t i = tid; i < topk; i += kSelThreads) o[i] = i < n ? (int32_t)i : -1;
+    return;
+  }
+  if (mm < m) {
+    m = mm;
+    if (m == 0) {
+      for (int64_t i = tid; i < topk; i += kSelThreads) o[i] = -1;
+      return;
+    }
+    radix_select<kSelThreads>(key_at, nslots, (uint32_t)m, lo, mx, hist, wave_cnt, s_sel, thr, need);
+  }
   // keys above the m-th best go to the bitmap, ties to a list; a
   // pathological tie at the boundary is settled exactly elsewhere
   const bool ok = bucketed ? output_bucketed_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel,
@@ -629,7 +644,7 @@ constexpr int kFbBlocks = 64;
 __global__ __launch_bounds__(kTopkThreads) void idx_fallback_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, int64_t S, int64_t p0, int64_t topk, const int32_t* __restrict__ fb,
-    float* __restrict__ scratch, int32_t* __restrict__ idx_out) {
+    float* __restrict__ scratch, int32_t* __restrict__ idx_out, DynK dyn) {
   __shared__ TopkShared sh;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -653,7 +668,7 @@ __global__ __launch_bounds__(kTopkThreads) void idx_fallback_kernel(
     }
     __threadfence_block();
     __syncthreads();
-    select_row(row, n, topk, idx_out + t * topk, sh);
+    select_row(row, n, topk, idx_out + t * topk, sh, dyn);
     __syncthreads();
   }
 }
@@ -673,7 +688,7 @@ bool index_select_supported(int64_t T, int64_t S) { return T >= 1 && S >= T && S
 
 hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t* k8, const float* ks,
                                int64_t T, int64_t S, int64_t topk, int32_t* idx_out, void* ws,
-                               bool force_fallback, hipStream_t st) {
+                               bool force_fallback, hipStream_t st, DynK dyn) {
   if (T <= 0) return hipSuccess;
   char* p = (char*)ws;
   auto take = [&](size_t x) {
@@ -709,9 +724,10 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
     attr = true;
   }
   idx_select_kernel<<<(unsigned)T, kSelThreads, lds, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, fb,
-                                                          force_fallback ? 1 : 0);
+                                                          force_fallback ? 1 : 0, dyn);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  idx_fallback_kernel<<<kFbBlocks, kTopkThreads, 0, st>>>(qf, qs, k8, ks, S, S - T, topk, fb, scratch, idx_out);
+  idx_fallback_kernel<<<kFbBlocks, kTopkThreads, 0, st>>>(qf, qs, k8, ks, S, S - T, topk, fb, scratch, idx_out,
+                                                          dyn);
   return hipGetLastError();
 }
 

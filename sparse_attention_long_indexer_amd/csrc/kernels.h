@@ -23,6 +23,16 @@ hipError_t launch_index_scores_decode(const uint8_t* qf, const float* qs, const 
                                       const float* ks, const int64_t* offsets, int64_t B,
                                       int64_t max_len, float* out, hipStream_t st);
 
+// Dynamic k (every selection path): a row keeps
+// min(n, k, max(k_min, #{scores > theta})) keys; theta = -inf keeps the
+// fixed min(n, k).
+struct DynK {
+  float theta;
+  int64_t k_min;
+};
+__host__ __device__ inline bool dyn_on(const DynK& d) { return d.theta > -__builtin_huge_valf(); }
+constexpr DynK kFixedK = {-__builtin_huge_valf(), 0};
+
 // topk.hip: rows are described by (row_off, n) pairs computed on device
 struct TopkRows {
   const float* scores;
@@ -36,7 +46,7 @@ struct TopkRows {
 };
 size_t topk_workspace_bytes(int64_t rows, int64_t max_n, int64_t k);
 hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k, int32_t* idx_out,
-                       int32_t* count_out, void* ws, hipStream_t st);
+                       int32_t* count_out, void* ws, hipStream_t st, DynK dyn = kFixedK);
 
 // index_select.hip: fused scores + top-k for a causal prefill chunk: query t
 // sits at position p0 + t and sees keys [0, p0 + t]; S = p0 + T keys
@@ -44,7 +54,7 @@ bool index_select_supported(int64_t T, int64_t S);
 size_t index_select_workspace_bytes(int64_t T, int64_t S);
 hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t* k8, const float* ks,
                                int64_t T, int64_t S, int64_t topk, int32_t* idx_out, void* ws,
-                               bool force_fallback, hipStream_t st);
+                               bool force_fallback, hipStream_t st, DynK dyn = kFixedK);
 
 // attn.hip
 struct AttnArgs {

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace dsa {
 
@@ -118,16 +119,42 @@ __device__ inline void radix_select(KeyAt key_at, int64_t n, uint32_t m, uint32_
   need = remaining;
 }
 
-// Exact top-k of one row p[0..n) by (score desc, index asc), written in
-// ascending index order to o[0..k) with -1 padding.  All kTopkThreads
+// Dynamic budget (DynK) of a row whose fixed selection of m keys has its
+// m-th best key at thr, counted over the keys key_at(0 .. nkeys) (all of the
+// row's keys above thr must be among them): m when the m best all lie above
+// theta, else max(k_min, #{keys > theta}) (<= m).  All threads must call.
+template <int NT, class KeyAt>
+__device__ inline int64_t dyn_budget(KeyAt key_at, int64_t nkeys, int64_t m, uint32_t thr, const DynK& dyn,
+                                     uint32_t* scan) {
+  if (!dyn_on(dyn)) return m;
+  const uint32_t tk = score_key(dyn.theta);
+  if (thr > tk) return m;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t c = 0;
+  for (int64_t i = tid; i < nkeys; i += NT) c += key_at(i) > tk ? 1u : 0u;
+  c = wave_sum(c);
+  __syncthreads();  // the caller's select may still read scan
+  if (lane == 0) scan[w] = c;
+  __syncthreads();
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) tot += scan[i];
+  __syncthreads();
+  const int64_t mm = (int64_t)tot > dyn.k_min ? (int64_t)tot : dyn.k_min;
+  return mm < m ? mm : m;
+}
+
+// Whole-row exact selection from fp32 scores p[0 .. n): the m best under
+// (score desc, index asc), m = min(n, k) or the row's dynamic budget, written
+// ascending to o[0 .. m) with o[m .. k) = -1.  Returns m.  All kTopkThreads
 // threads of the block call it; `sh` is block-shared scratch.
-__device__ inline void select_row(const float* __restrict__ p, int64_t n, int64_t k, int32_t* __restrict__ o,
-                                  TopkShared& sh) {
+__device__ inline int64_t select_row(const float* __restrict__ p, int64_t n, int64_t k, int32_t* __restrict__ o,
+                                     TopkShared& sh, DynK dyn = kFixedK) {
   const int tid = threadIdx.x;
-  const int64_t m = n < k ? n : k;
-  if (n <= k) {  // every key is kept
+  int64_t m = n < k ? n : k;
+  if (n <= k && !dyn_on(dyn)) {  // every key is kept
     for (int64_t i = tid; i < k; i += kTopkThreads) o[i] = i < n ? (int32_t)i : -1;
-    return;
+    return m;
   }
   // key range of the row
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -150,9 +177,22 @@ __device__ inline void select_row(const float* __restrict__ p, int64_t n, int64_
     mx = max(mx, sh.hist[i]);
   }
   __syncthreads();
-  uint32_t thr, need;
-  radix_select<kTopkThreads>([&](int64_t i) { return score_key(p[i]); }, n, (uint32_t)m, mn, mx, sh.hist,
-                             sh.wave_cnt, sh.sel, thr, need);
+  auto key_at = [&](int64_t i) { return score_key(p[i]); };
+  uint32_t thr = mn, need = 0;
+  if (n > k) radix_select<kTopkThreads>(key_at, n, (uint32_t)m, mn, mx, sh.hist, sh.wave_cnt, sh.sel, thr, need);
+  const int64_t mm = dyn_budget<kTopkThreads>(key_at, n, m, thr, dyn, sh.wave_cnt);
+  if (n <= k && mm == m) {  // dynamic budget keeps the whole short row
+    for (int64_t i = tid; i < k; i += kTopkThreads) o[i] = i < n ? (int32_t)i : -1;
+    return m;
+  }
+  if (mm < m) {
+    m = mm;
+    if (m == 0) {
+      for (int64_t i = tid; i < k; i += kTopkThreads) o[i] = -1;
+      return 0;
+    }
+    radix_select<kTopkThreads>(key_at, n, (uint32_t)m, mn, mx, sh.hist, sh.wave_cnt, sh.sel, thr, need);
+  }
 
   // ordered selection: keys > thr, and the first `need` keys == thr
   uint32_t carry_eq = 0, carry_sel = 0;
@@ -171,6 +211,7 @@ __device__ inline void select_row(const float* __restrict__ p, int64_t n, int64_
     carry_sel += tot_sel;
   }
   for (int64_t i = m + tid; i < k; i += kTopkThreads) o[i] = -1;
+  return m;
 }
 
 // Ascending output from a candidate list: given thr / need from radix_select

@@ -49,12 +49,12 @@ __device__ __forceinline__ RowView topk_row_view(const TopkRows& R, int64_t row)
 
 __global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(TopkRows R, int64_t k,
                                                                   int32_t* __restrict__ idx_out,
-                                                                  int32_t* __restrict__ count_out) {
+                                                                  int32_t* __restrict__ count_out, DynK dyn) {
   __shared__ TopkShared sh;
   const int64_t row = blockIdx.x;
   const RowView rv = topk_row_view(R, row);
-  if (count_out && threadIdx.x == 0) count_out[row] = (int32_t)(rv.n < k ? rv.n : k);
-  select_row(rv.p, rv.n, k, idx_out + row * k, sh);
+  const int64_t m = select_row(rv.p, rv.n, k, idx_out + row * k, sh, dyn);
+  if (count_out && threadIdx.x == 0) count_out[row] = (int32_t)m;
 }
 
 // ---- candidate path for few long rows --------------------------------------
@@ -211,7 +211,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
                                                                        const uint2* __restrict__ cand,
                                                                        const int32_t* __restrict__ cnt,
                                                                        int32_t* __restrict__ idx_out,
-                                                                       int32_t* __restrict__ count_out) {
+                                                                       int32_t* __restrict__ count_out,
+                                                                       DynK dyn) {
   constexpr int NT = kTopkThreads;
   extern __shared__ __align__(16) uint32_t sm[];
   uint2* cl = (uint2*)sm;                  // [kCandCap] (key, position)
@@ -222,17 +223,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t row = blockIdx.x;
   const RowView rv = topk_row_view(R, row);
-  const int64_t n = rv.n, m = n < k ? n : k;
+  const int64_t n = rv.n;
+  int64_t m = n < k ? n : k;
   int32_t* o = idx_out + row * k;
-  if (count_out && tid == 0) count_out[row] = (int32_t)m;
-  if (n <= k) {
-    for (int64_t i = tid; i < k; i += NT) o[i] = i < n ? (int32_t)i : -1;
-    return;
-  }
   const uint32_t tk = tau[row];
   const int c = cnt[row];
-  if (c > kCandCap || (tk != 0u && c < m)) {  // block-uniform
-    select_row(rv.p, n, k, o, sh);
+  if (n <= k || c > kCandCap || (tk != 0u && c < m)) {  // block-uniform
+    m = select_row(rv.p, n, k, o, sh, dyn);
+    if (count_out && tid == 0) count_out[row] = (int32_t)m;
     return;
   }
   const bool bucketed = n > kCandBitmapN;
@@ -263,16 +261,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
   }
   __syncthreads();
   uint32_t thr, need;
-  radix_select<NT>([&](int64_t e) { return cl[e].x; }, c, (uint32_t)m, tk != 0u ? tk : mn, mx, sh.hist,
-                   sh.wave_cnt, sh.sel, thr, need);
+  const uint32_t lo = tk != 0u ? tk : mn;
+  auto key_at = [&](int64_t e) { return cl[e].x; };
+  radix_select<NT>(key_at, c, (uint32_t)m, lo, mx, sh.hist, sh.wave_cnt, sh.sel, thr, need);
+  // dynamic k: every key above theta is a candidate once the m-th best is
+  // at or below theta (the m-th best is >= tau)
+  const int64_t mm = dyn_budget<NT>(key_at, c, m, thr, dyn, sh.wave_cnt);
+  if (mm < m) {
+    m = mm;
+    if (m == 0) {
+      for (int64_t i = tid; i < k; i += NT) o[i] = -1;
+      if (count_out && tid == 0) count_out[row] = 0;
+      return;
+    }
+    radix_select<NT>(key_at, c, (uint32_t)m, lo, mx, sh.hist, sh.wave_cnt, sh.sel, thr, need);
+  }
   const bool ok = bucketed ? output_bucketed_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, s_tie, kCandMaxTies,
                                                                &s_ntie, sh.wave_cnt, o)
                           : output_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie,
                                                        kCandMaxTies, &s_ntie, sh.wave_cnt, o);
   if (!ok) {
     __syncthreads();
-    select_row(rv.p, n, k, o, sh);  // a boundary tie too long for the list
+    m = select_row(rv.p, n, k, o, sh, dyn);  // a boundary tie too long for the list
   }
+  if (count_out && tid == 0) count_out[row] = (int32_t)m;
 }
 
 struct CandWs {
@@ -301,10 +313,10 @@ size_t topk_workspace_bytes(int64_t rows, int64_t max_n, int64_t k) {
 }
 
 hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k, int32_t* idx_out,
-                       int32_t* count_out, void* ws, hipStream_t st) {
+                       int32_t* count_out, void* ws, hipStream_t st, DynK dyn) {
   if (rows <= 0) return hipSuccess;
   if (!ws || !topk_use_candidates(rows, max_n, k)) {
-    topk_radix_kernel<<<(unsigned)rows, kTopkThreads, 0, st>>>(r, k, idx_out, count_out);
+    topk_radix_kernel<<<(unsigned)rows, kTopkThreads, 0, st>>>(r, k, idx_out, count_out, dyn);
     return hipGetLastError();
   }
   CandWs c;
@@ -329,7 +341,7 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
                            : (size_t)((bm + 31) / 32);
   const size_t lds = (size_t)kCandCap * 8 + words * 4;
   topk_cand_select_kernel<<<(unsigned)rows, kTopkThreads, lds, st>>>(r, k, c.tau, c.cand, c.cnt, idx_out,
-                                                                     count_out);
+                                                                     count_out, dyn);
   return hipGetLastError();
 }
 

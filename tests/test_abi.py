@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 2
+    assert lib.dsa_abi_version() == 3
     for s in range(7):
         assert lib.dsa_status_str(s)
     assert lib.dsa_status_str(99) == b"unknown status"
@@ -77,6 +77,19 @@ def test_topk_validation(lib):
     assert f(a, 9, 4, 10, None, 8, a, None, None, 0, None) == 2            # ld < S
     assert f(a, 10, 4, 10, None, 8, None, None, None, 0, None) == 1        # no output
     assert f(a, 10, 0, 10, None, 8, None, None, None, 0, None) == 0        # no rows
+
+
+def test_topk_dynamic_validation(lib):
+    f = lib.dsa_topk_dynamic
+    a = _vp(0x10000)
+    nan = ctypes.c_float(float("nan"))
+    th = ctypes.c_float(0.5)
+    assert f(a, 10, 4, 10, None, 8, 9, th, a, None, None, 0, None) == 2     # k_min > k_max
+    assert f(a, 10, 4, 10, None, 8, -1, th, a, None, None, 0, None) == 2    # k_min < 0
+    assert f(a, 10, 4, 10, None, 8, 2, nan, a, None, None, 0, None) == 2    # theta NaN
+    assert f(a, 10, 4, 10, None, 0, 0, th, a, None, None, 0, None) == 2     # k_max = 0
+    assert f(a, 10, 4, 10, None, 8, 2, th, None, None, None, 0, None) == 1  # no output
+    assert f(a, 10, 0, 10, None, 8, 2, th, None, None, None, 0, None) == 0  # no rows
 
 
 def test_attn_validation(lib):
@@ -125,7 +138,24 @@ def test_forward_validation(lib):
     assert 0 < n16 < n4k
     assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p), n4k - 1, None) == 5
     assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p + 8), n4k, None) == 5
+    # a later chunk of a prefill sees more keys: a larger workspace
+    a.q_offset = 1 << 20
+    assert lib.dsa_forward_workspace_size(ctypes.byref(a)) > n4k
+    a.q_offset = -1
+    assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p), 1 << 40, None) == 2
+    a.q_offset = (1 << 31) - 4096    # positions past int32
+    assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p), 1 << 40, None) == 2
+    a.q_offset = 0
+    a.flags = B.DSA_FLAG_DYNAMIC_K
+    a.dyn_theta, a.dyn_k_min = 0.5, 65           # k_min above topk
+    assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p), 1 << 40, None) == 2
+    a.dyn_theta, a.dyn_k_min = float("nan"), 1
+    assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p), 1 << 40, None) == 2
+    a.flags = 0
     a.mode = B.DSA_MODE_DECODE
     a.seq_offsets = None
     a.T, a.total_keys, a.max_len = 4, 100, 50
     assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p), 1 << 30, None) == 1
+    a.q_offset = 3                               # decode takes no query offset
+    assert lib.dsa_forward(ctypes.byref(a), None, _vp(p), _vp(p), 1 << 30, None) == 2
+    a.q_offset = 0
