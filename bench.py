@@ -279,6 +279,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="row-time budget of the CPU baseline")
     ap.add_argument("--chunk", type=int, default=131072, help="queries per chunk of the 2^20-token prefill")
+    ap.add_argument("--dynamic-theta", type=float, default=None,
+                    help="per-query k: keep the keys scoring above this (within [--dynamic-kmin, k])")
+    ap.add_argument("--dynamic-kmin", type=int, default=0)
     ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
                     help="only run the counter-profile sequence (a 2 GiB copy, then N attention launches)")
     args = ap.parse_args()
@@ -306,7 +309,7 @@ def main():
     L, k = spec.L, spec.topk
     out = torch.empty((L, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
     idx = torch.empty((L, k), dtype=torch.int32, device=dev)
-    fa = B.forward_args(x, k, spec.scale, spec.Dv)
+    fa = B.forward_args(x, k, spec.scale, spec.Dv, dyn_theta=args.dynamic_theta, dyn_k_min=args.dynamic_kmin)
     ws = torch.empty(max(B.dsa_forward_workspace_size(fa), 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -339,6 +342,9 @@ def main():
     torch.cuda.synchronize()
     attn_ms = ev0.elapsed_time(ev1) / reps
     flops, pairs = attn_flops(L, k, spec.H, spec.Dk, spec.Dv)
+    if args.dynamic_theta is not None:  # the pairs the per-query budgets kept
+        pairs = int((idx >= 0).sum())
+        flops = 2.0 * spec.H * (spec.Dk + spec.Dv) * pairs
     achieved = flops / (attn_ms * 1e-3) / 1e12
     sha = kernel_source_sha(["attn.hip", "common.h", "kernels.h"])
     traffic = load_traffic("attn_bf16_kernel<576,512,8>", sha)
@@ -364,6 +370,10 @@ def main():
                    "batch": 1, "index_dim": 128},
         "roofline": roof, "roofline_indexer": roof_idx,
     }
+    if args.dynamic_theta is not None:
+        result["metric"] = "DSA prefill tokens/s at L=128K, dynamic k (theta, k_min .. 2048)"
+        result["config"]["dynamic_k"] = {"theta": args.dynamic_theta, "k_min": args.dynamic_kmin,
+                                         "mean_kept": round(pairs / L, 2)}
     del out, idx, ws
 
     if not args.no_decode:
