@@ -156,6 +156,53 @@ def attend(q_heads: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: f
     return o, (zmax + np.log(den))[:, 0]
 
 
+def attend_backward(q_heads: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: float,
+                    d_out: np.ndarray):
+    """Gradients of `attend` for one query in fp64 (the sparse training stage
+    of the write-up, section 4.1, trains through attention over the selected
+    keys).  With z = scale q k^T, p = softmax(z), o = p v and the incoming
+    gradient dO of o:
+      dv = p^T dO;   dp = dO v^T;   dz = p * (dp - rowsum(dO * o));
+      dq = scale dz k;   dk = scale dz^T q.
+    Returns (dq [H, Dk], dk [n, Dk], dv [n, Dv])."""
+    q = np.asarray(q_heads, np.float64)
+    kr = np.asarray(k_rows, np.float64)
+    vr = np.asarray(v_rows, np.float64)
+    do = np.asarray(d_out, np.float64)
+    z = scale * (q @ kr.T)
+    e = np.exp(z - np.max(z, axis=1, keepdims=True))
+    p = e / np.sum(e, axis=1, keepdims=True)
+    o = p @ vr
+    dv = p.T @ do
+    dp = do @ vr.T
+    dz = p * (dp - np.sum(do * o, axis=1, keepdims=True))
+    return scale * (dz @ kr), scale * (dz.T @ q), dv
+
+
+def sparse_attn_backward(q, kv, idx, scale: float, Dv: int, d_out, rows=None):
+    """Backward of sparse MQA attention over a shared latent KV row per key
+    (K = kv[:, :Dk], V = kv[:, :Dv]): dq [T, H, Dk] and dkv [S, Dk], the sum
+    over every query that selected a key of its dk, plus its dv in the first
+    Dv columns.  `rows` restricts the queries (dq of the others stays 0 and
+    they add nothing to dkv).  Inputs in the library's storage formats."""
+    qa = as_f64(q)
+    kva = as_f64(kv)
+    doa = as_f64(d_out)
+    T = qa.shape[0]
+    dq = np.zeros_like(qa)
+    dkv = np.zeros_like(kva)
+    for t in (range(T) if rows is None else rows):
+        sel = np.asarray(idx[t])
+        sel = sel[: np.argmax(sel < 0)] if np.any(sel < 0) else sel
+        if sel.shape[0] == 0:
+            continue
+        krows = kva[sel]
+        dq[t], dk, dv = attend_backward(qa[t], krows, krows[:, :Dv], scale, doa[t])
+        np.add.at(dkv, sel, dk)
+        np.add.at(dkv[:, :Dv], sel, dv)
+    return dq, dkv
+
+
 # ---------------------------------------------------------- whole forward ---
 
 class PrefillOracle:

@@ -421,6 +421,72 @@ def pin_decode_equals_prefill_row(od, oc):
         assert np.array_equal(i1, i2) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def pin_attend_backward_autograd_and_differences(od, oc):
+    """Gradients of attention against torch autograd of an independently
+    written fp64 forward, and against central differences of the oracle's own
+    forward."""
+    rng = np.random.default_rng(21)
+    for H, n, Dk, Dv in ((3, 5, 8, 6), (2, 1, 4, 4), (4, 9, 12, 12)):
+        q = rng.standard_normal((H, Dk))
+        kk = rng.standard_normal((n, Dk))
+        vv = rng.standard_normal((n, Dv))
+        do = rng.standard_normal((H, Dv))
+        scale = 0.37
+        dq, dk, dv = od.attend_backward(q, kk, vv, scale, do)
+        tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, kk, vv))
+        w = torch.softmax(scale * tq @ tk.T, dim=1)
+        (w @ tv * torch.tensor(do)).sum().backward()
+        assert np.allclose(dq, tq.grad.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(dk, tk.grad.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(dv, tv.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+        def loss(qq, kr, vr):
+            return float(np.sum(od.attend(qq, kr, vr, scale)[0] * do))
+
+        h = 1e-6
+        for arr, grad, which in ((q, dq, 0), (kk, dk, 1), (vv, dv, 2)):
+            for _ in range(4):
+                i = tuple(rng.integers(0, d) for d in arr.shape)
+                a1, a2 = arr.copy(), arr.copy()
+                a1[i] += h
+                a2[i] -= h
+                args1 = [q, kk, vv]
+                args2 = [q, kk, vv]
+                args1[which], args2[which] = a1, a2
+                fd = (loss(*args1) - loss(*args2)) / (2 * h)
+                assert abs(fd - grad[i]) <= 1e-6 * (1 + abs(fd)), (which, i, fd, grad[i])
+
+
+def pin_sparse_attn_backward_scatter(od, oc):
+    """The sparse backward's shared-latent scatter: equal to the dense-form
+    gradient of the sum over queries, with K and V both slices of one
+    leaf tensor, by torch autograd."""
+    rng = np.random.default_rng(23)
+    T, H, S, Dk, Dv, k = 5, 2, 11, 8, 6, 4
+    q = rng.standard_normal((T, H, Dk))
+    kv = rng.standard_normal((S, Dk))
+    do = rng.standard_normal((T, H, Dv))
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        m = [4, 3, 1, 0, 4][t]
+        idx[t, :m] = np.sort(rng.choice(S, m, replace=False))
+    dq, dkv = od.sparse_attn_backward(q, kv, idx, 0.5, Dv, do)
+    tq = torch.tensor(q, requires_grad=True)
+    tkv = torch.tensor(kv, requires_grad=True)
+    total = 0
+    for t in range(T):
+        sel = [int(s) for s in idx[t] if s >= 0]
+        if not sel:
+            continue
+        rows = tkv[sel]
+        w = torch.softmax(0.5 * tq[t] @ rows.T, dim=1)
+        total = total + (w @ rows[:, :Dv] * torch.tensor(do[t])).sum()
+    total.backward()
+    assert np.allclose(dq, tq.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dkv, tkv.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.all(dq[3] == 0)   # a query with no selected key
+
+
 def pin_page_constants(od, oc):
     """The write-up's constants and its ~3% indexer share at L=128K, checked
     against the 128K workload's shapes (a shape pin, not a parity pin)."""
@@ -446,4 +512,5 @@ ALL_PINS = [
     pin_requant_closed_forms, pin_scores_one_hot, pin_brute_force, pin_prefill_chunk_brute_force,
     pin_scores_causal_relu, pin_topk_properties, pin_dynamic_k,
     pin_attend_special_cases, pin_sparse_equals_dense, pin_decode_equals_prefill_row, pin_page_constants,
+    pin_attend_backward_autograd_and_differences, pin_sparse_attn_backward_scatter,
 ]

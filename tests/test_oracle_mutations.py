@@ -157,7 +157,37 @@ def _dynamic_k_no_floor(scores, k_max, k_min, theta):
     return min(n, k_max, int(np.count_nonzero(np.asarray(scores) > theta)))
 
 
+def _bwd_no_rowsum(q, k, v, scale, do):
+    q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
+    z = scale * (q @ k.T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dz = p * (do @ v.T)
+    return scale * (dz @ k), scale * (dz.T @ q), p.T @ do
+
+
+def _bwd_dq_unscaled(q, k, v, scale, do):
+    dq, dk, dv = _orig_bwd(q, k, v, scale, do)
+    return dq / scale, dk, dv
+
+
+_orig_bwd = od.attend_backward
+
+
+def _sparse_bwd_no_dv(q, kv, idx, scale, Dv, d_out, rows=None):
+    qa, kva, doa = od.as_f64(q), od.as_f64(kv), od.as_f64(d_out)
+    dq, dkv = np.zeros_like(qa), np.zeros_like(kva)
+    for t in range(qa.shape[0]):
+        sel = np.asarray([s for s in idx[t] if s >= 0], np.int64)
+        if sel.shape[0]:
+            dq[t], dk, _ = _orig_bwd(qa[t], kva[sel], kva[sel][:, :Dv], scale, doa[t])
+            np.add.at(dkv, sel, dk)
+    return dq, dkv
+
 MUTATIONS = {
+    "attn_bwd_dropped_rowsum": (od, "attend_backward", _bwd_no_rowsum),
+    "attn_bwd_dq_unscaled": (od, "attend_backward", _bwd_dq_unscaled),
+    "sparse_bwd_dropped_dv_scatter": (od, "sparse_attn_backward", _sparse_bwd_no_dv),
     "dynamic_k_counts_ties_at_theta": (od, "dynamic_k", _dynamic_k_ge),
     "dynamic_k_ignores_k_min": (od, "dynamic_k", _dynamic_k_no_floor),
     "prefill_chunk_ignores_offset": (od.PrefillOracle, "scores_row", _chunk_ignores_offset),
