@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 #define DSA_INDEX_DIM 128   /* index-key width, write-up section 2.2 */
 #define DSA_MAX_TOPK 4096
 
@@ -181,6 +181,37 @@ dsa_status_t dsa_sparse_attn(const void* q, int64_t T, int64_t H, int64_t Dk, ds
                              const void* kv, int64_t ld_kv, const void* v, int64_t ld_v, int64_t Dv,
                              int64_t S, const int32_t* idx, int64_t k, float scale, void* out,
                              float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of dsa_sparse_attn for the sparse training stage (write-up
+ * section 4.1: after the dense warm-up the whole model trains through
+ * attention over the selected keys).  Shared latent KV only (v = NULL in the
+ * forward: K = kv[s, :Dk], V = kv[s, :Dv]).  With P the forward's softmax
+ * weights (from lse_in) and dO = d_out:
+ *   dS[t,h,j] = scale P[t,h,j] (dO[t,h] . V_j - dO[t,h] . out[t,h])
+ *   dq[t,h]  = sum_j dS[t,h,j] K_j                       (written)
+ *   dkv[s]  += sum over (t, h, j) with idx[t][j] = s of
+ *              dS[t,h,j] q[t,h]  (all Dk columns)
+ *            + P[t,h,j] dO[t,h]  (the first Dv columns)  (accumulated)
+ * The caller zeroes dkv before the first call; dkv may then collect the
+ * gradients of several calls.  Accumulation order across queries is not
+ * fixed (hardware float atomics), so dkv is reproducible to rounding only.
+ *
+ * q, out, d_out, dq  device bf16 [T][H][Dk], [T][H][Dv], [T][H][Dv], [T][H][Dk]
+ * kv        device bf16 [S][ld_kv]; idx device int32 [T][k] as for the forward
+ * lse_in    device fp32 [T][H]: the forward's lse_out
+ * dkv       device fp32 [S][ld_dkv], ld_dkv >= Dk
+ * Supported: dtype = DSA_BF16, H = 128, Dk = 576, Dv = 512, k a multiple of
+ * 32 up to DSA_MAX_TOPK; otherwise DSA_ERR_UNSUPPORTED.
+ * Workspace: dsa_sparse_attn_bwd_workspace_size(T, H, k) bytes (P and dS of
+ * a chunk of queries in bf16; the call walks the queries in chunks).
+ */
+size_t dsa_sparse_attn_bwd_workspace_size(int64_t T, int64_t H, int64_t k);
+dsa_status_t dsa_sparse_attn_bwd(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dtype_t dtype,
+                                 const void* kv, int64_t ld_kv, int64_t Dv, int64_t S, const int32_t* idx,
+                                 int64_t k, float scale, const void* out, const float* lse_in,
+                                 const void* d_out, void* dq, float* dkv, int64_t ld_dkv, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /*
  * Whole forward: fold, scores, top-k and sparse attention.

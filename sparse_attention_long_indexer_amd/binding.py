@@ -25,12 +25,12 @@ DSA_FLAG_FORCE_FALLBACK = 4
 DSA_FLAG_DYNAMIC_K = 8
 INDEX_DIM = 128
 MAX_TOPK = 4096
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTED = [
     "dsa_abi_version", "dsa_status_str", "dsa_fold_index_query", "dsa_index_scores",
     "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_dynamic", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
-    "dsa_forward_workspace_size", "dsa_forward",
+    "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd", "dsa_forward_workspace_size", "dsa_forward",
 ]
 
 
@@ -72,6 +72,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsa_sparse_attn_workspace_size": ([c_i64, c_i64, c_i64, c_i64, c_int], c_sz),
         "dsa_sparse_attn": ([c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64,
                              c_f, c_vp, c_vp, c_vp, c_sz, c_vp], c_int),
+        "dsa_sparse_attn_bwd_workspace_size": ([c_i64, c_i64, c_i64], c_sz),
+        "dsa_sparse_attn_bwd": ([c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_f,
+                                 c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_sz, c_vp], c_int),
         "dsa_forward_workspace_size": ([ctypes.POINTER(ForwardArgs)], c_sz),
         "dsa_forward": ([ctypes.POINTER(ForwardArgs), c_vp, c_vp, c_vp, c_sz, c_vp], c_int),
     }
@@ -189,6 +192,24 @@ def dsa_sparse_attn(q, kv, idx, scale, v=None, Dv=None, out=None, lse_out=None, 
         _p(q), T, H, Dk, dt, _p(kv), kv.stride(0), _p(v), v.stride(0) if v is not None else 0, Dv, S, _p(idx), k,
         ctypes.c_float(scale), _p(out), _p(lse_out), _p(ws), wsb, _stream(stream)))
     return out
+
+
+def dsa_sparse_attn_bwd(q, kv, idx, scale, out, lse, d_out, Dv, dq=None, dkv=None, stream=None):
+    """dq (bf16, written) and dkv (fp32, accumulated; zeroed here when not
+    given) of the shared-latent sparse attention."""
+    T, H, Dk = q.shape
+    S = kv.shape[0]
+    k = idx.shape[1]
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dkv is None:
+        dkv = torch.zeros((S, Dk), dtype=torch.float32, device=q.device)
+    wsb = lib().dsa_sparse_attn_bwd_workspace_size(T, H, k)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
+    _check("dsa_sparse_attn_bwd", lib().dsa_sparse_attn_bwd(
+        _p(q), T, H, Dk, _dtype_code(q), _p(kv), kv.stride(0), Dv, S, _p(idx), k, ctypes.c_float(scale), _p(out),
+        _p(lse), _p(d_out), _p(dq), _p(dkv), dkv.stride(0), _p(ws), ws.numel(), _stream(stream)))
+    return dq, dkv
 
 
 def forward_args(x: dict, topk: int, scale: float, Dv: int, mode: int = DSA_MODE_PREFILL, flags: int = 0,

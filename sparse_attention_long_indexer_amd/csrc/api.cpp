@@ -297,6 +297,48 @@ dsa_status_t dsa_sparse_attn(const void* q, int64_t T, int64_t H, int64_t Dk, ds
   }
 }
 
+size_t dsa_sparse_attn_bwd_workspace_size(int64_t T, int64_t H, int64_t k) {
+  if (T < 1 || H != 128 || k < 1) return 0;
+  return attn_bwd_workspace_bytes(T, k);
+}
+
+dsa_status_t dsa_sparse_attn_bwd(const void* q, int64_t T, int64_t H, int64_t Dk, dsa_dtype_t dtype,
+                                 const void* kv, int64_t ld_kv, int64_t Dv, int64_t S, const int32_t* idx,
+                                 int64_t k, float scale, const void* out, const float* lse_in,
+                                 const void* d_out, void* dq, float* dkv, int64_t ld_dkv, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  try {
+    if (T < 0 || S < 1 || k < 1 || ld_kv < Dk || ld_dkv < Dk || Dv > Dk) return DSA_ERR_SHAPE;
+    if (dtype != DSA_BF16) return dtype == DSA_F32 ? DSA_ERR_UNSUPPORTED : DSA_ERR_DTYPE;
+    if (!attn_bwd_supported(H, Dk, Dv, k)) return DSA_ERR_UNSUPPORTED;
+    if (T == 0) return DSA_OK;
+    if (!q || !kv || !idx || !out || !lse_in || !d_out || !dq || !dkv) return DSA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(d_out, 16) || (ld_kv * 2) % 16)
+      return DSA_ERR_SHAPE;
+    const size_t need = attn_bwd_workspace_bytes(T, k);
+    if (ws_bytes < need || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
+    DSA_TRY(check_device());
+    BwdArgs a{};
+    a.q = q;
+    a.kv = kv;
+    a.ld_kv = ld_kv;
+    a.idx = idx;
+    a.S = S;
+    a.T = T;
+    a.k = k;
+    a.scale = scale;
+    a.out = out;
+    a.lse = lse_in;
+    a.dout = d_out;
+    a.dq = dq;
+    a.dkv = dkv;
+    a.ld_dkv = ld_dkv;
+    return from_hip(launch_attn_bwd(a, ws, as_stream(stream)));
+  } catch (...) {
+    return DSA_ERR_DEVICE;
+  }
+}
+
 size_t dsa_forward_workspace_size(const dsa_forward_args* a) {
   if (!a || check_forward(a) != DSA_OK) return 0;
   const FwdPlan p = plan_forward(a, true);

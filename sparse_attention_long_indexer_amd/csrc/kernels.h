@@ -56,6 +56,27 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
                                int64_t T, int64_t S, int64_t topk, int32_t* idx_out, void* ws,
                                bool force_fallback, hipStream_t st, DynK dyn = kFixedK);
 
+// attn_bwd.hip: backward of the bf16 sparse attention with a shared latent
+// KV row per key (H = 128, Dk = 576, Dv = 512)
+struct BwdArgs {
+  const void* q;        // [T][H][Dk] bf16
+  const void* kv;       // [S][ld_kv] bf16
+  int64_t ld_kv;
+  const int32_t* idx;   // [T][k]
+  int64_t S, T, k;
+  float scale;
+  const void* out;      // [T][H][Dv] bf16, the forward's output
+  const float* lse;     // [T][H], the forward's log-sum-exp (natural log)
+  const void* dout;     // [T][H][Dv] bf16
+  void* dq;             // [T][H][Dk] bf16 (written)
+  float* dkv;           // [S][ld_dkv] fp32 (accumulated)
+  int64_t ld_dkv;
+};
+bool attn_bwd_supported(int64_t H, int64_t Dk, int64_t Dv, int64_t k);
+int64_t attn_bwd_chunk(int64_t T, int64_t k);
+size_t attn_bwd_workspace_bytes(int64_t T, int64_t k);
+hipError_t launch_attn_bwd(const BwdArgs& a, void* ws, hipStream_t st);
+
 // attn.hip
 struct AttnArgs {
   const void* q;        // [T][H][Dk]

@@ -226,6 +226,14 @@ def make_scores(T: int, S: int, seed: int = 0, device="cpu", q_pos: Optional[tor
     return x.to(device)
 
 
+def make_grad(shape, seed: int = 0, device="cpu", dtype=torch.bfloat16) -> torch.Tensor:
+    """An incoming gradient (dLoss/dout) for the backward pass: N(0,1)
+    entries stored as `dtype`."""
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(seed * 6_151 + 101)
+    return _randn(tuple(shape), g, torch.device(device), 1.0, dtype)
+
+
 def make_selection(T: int, S: int, k: int, seed: int = 0, device="cpu", min_valid: int = 0) -> torch.Tensor:
     """int32 [T][k] rows of ascending distinct key indices in [0, S), each row
     holding a random number (>= min_valid) of valid entries followed by -1."""

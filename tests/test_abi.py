@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 3
+    assert lib.dsa_abi_version() == 4
     for s in range(7):
         assert lib.dsa_status_str(s)
     assert lib.dsa_status_str(99) == b"unknown status"
@@ -90,6 +90,27 @@ def test_topk_dynamic_validation(lib):
     assert f(a, 10, 4, 10, None, 0, 0, th, a, None, None, 0, None) == 2     # k_max = 0
     assert f(a, 10, 4, 10, None, 8, 2, th, None, None, None, 0, None) == 1  # no output
     assert f(a, 10, 0, 10, None, 8, 2, th, None, None, None, 0, None) == 0  # no rows
+
+
+def test_attn_bwd_validation(lib):
+    f = lib.dsa_sparse_attn_bwd
+    p = _vp(0x100000)
+    sc = ctypes.c_float(0.04)
+    args = dict(q=p, T=4, H=128, Dk=576, dt=B.DSA_BF16, kv=p, ldkv=576, Dv=512, S=100, idx=p, k=64, sc=sc, out=p,
+                lse=p, do=p, dq=p, dkv=p, lddkv=576, ws=p, wsb=1 << 30, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+    assert call(dt=B.DSA_F32) == 4          # fp32 not supported
+    assert call(dt=7) == 3                  # not a dtype
+    assert call(H=64) == 4                  # head count
+    assert call(k=100) == 4                 # k not a multiple of 32
+    assert call(ldkv=500) == 2              # ld_kv < Dk
+    assert call(dq=None) == 1
+    assert call(wsb=16) == 5
+    assert call(T=0) == 0
+    assert lib.dsa_sparse_attn_bwd_workspace_size(4, 128, 64) > 0
 
 
 def test_attn_validation(lib):
