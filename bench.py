@@ -179,6 +179,36 @@ def decode_step_stats(B, gen, torch, dev, ds, lengths=None, reps=20):
                          "note": "warm caches; whole decode step"}}
 
 
+def backward_stats(B, torch, spec, x, idx, out, pairs, reps=3):
+    """Time dsa_sparse_attn_bwd over the forward's selection with HIP events
+    on the launch stream; algorithmic FLOPs per selected pair: S and dP
+    recomputed, dq, dk and dv, 2 H (3 Dk + 2 Dv)."""
+    from sparse_attention_long_indexer_amd import inputs as gen
+    L = x["q"].shape[0]
+    dev = x["q"].device
+    lse = torch.empty((L, spec.H), dtype=torch.float32, device=dev)
+    B.dsa_sparse_attn(x["q"], x["kv"], idx, spec.scale, Dv=spec.Dv, out=out, lse_out=lse)
+    d_out = gen.make_grad((L, spec.H, spec.Dv), seed=5, device=dev)
+    dq = torch.empty_like(x["q"])
+    dkv = torch.zeros((x["kv"].shape[0], spec.Dk), dtype=torch.float32, device=dev)
+    B.dsa_sparse_attn_bwd(x["q"], x["kv"], idx, spec.scale, out, lse, d_out, spec.Dv, dq=dq, dkv=dkv)
+    st = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(st)
+    for _ in range(reps):
+        B.dsa_sparse_attn_bwd(x["q"], x["kv"], idx, spec.scale, out, lse, d_out, spec.Dv, dq=dq, dkv=dkv)
+    ev1.record(st)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    flops = 2.0 * spec.H * (3 * spec.Dk + 2 * spec.Dv) * pairs
+    achieved = flops / (ms * 1e-3) / 1e12
+    log(f"backward {ms:.2f} ms = {achieved:.1f} TFLOP/s")
+    del d_out, dq, dkv, lse
+    return {"ms": round(ms, 3), "selected_pairs": pairs, "algorithmic_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}}
+
+
 def bench_long(args, B, gen, torch, dev):
     """The 2^20-token prefill as chunks of C queries (each chunk attends over
     the keys of every earlier chunk and its own), then a 64-sequence decode
@@ -282,6 +312,8 @@ def main():
     ap.add_argument("--dynamic-theta", type=float, default=None,
                     help="per-query k: keep the keys scoring above this (within [--dynamic-kmin, k])")
     ap.add_argument("--dynamic-kmin", type=int, default=0)
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the sparse attention backward (dq, dkv) over the prefill's selection")
     ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
                     help="only run the counter-profile sequence (a 2 GiB copy, then N attention launches)")
     args = ap.parse_args()
@@ -374,6 +406,8 @@ def main():
         result["metric"] = "DSA prefill tokens/s at L=128K, dynamic k (theta, k_min .. 2048)"
         result["config"]["dynamic_k"] = {"theta": args.dynamic_theta, "k_min": args.dynamic_kmin,
                                          "mean_kept": round(pairs / L, 2)}
+    if args.backward:
+        result["backward"] = backward_stats(B, torch, spec, x, idx, out, pairs, reps=max(2, args.steps))
     del out, idx, ws
 
     if not args.no_decode:
