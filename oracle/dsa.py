@@ -203,6 +203,56 @@ def sparse_attn_backward(q, kv, idx, scale: float, Dv: int, d_out, rows=None):
     return dq, dkv
 
 
+# ------------------------------------- section 4.1: indexer alignment (KL) ---
+
+def attention_target_row(q_heads: np.ndarray, k_rows: np.ndarray, scale: float) -> np.ndarray:
+    """The dense model's attention distribution of one query over its keys,
+    summed over the heads and L1-normalised (reading R21): the mean over
+    heads of softmax_s(scale q_h . k_s)."""
+    q = np.asarray(q_heads, np.float64)
+    z = scale * (q @ np.asarray(k_rows, np.float64).T)
+    e = np.exp(z - np.max(z, axis=1, keepdims=True))
+    return np.mean(e / np.sum(e, axis=1, keepdims=True), axis=0)
+
+
+def indexer_kl(q_idx, k_idx, w, q, kv, scale: float, Dk: int, rows=None):
+    """KL alignment of the lightning indexer to the dense attention (dense
+    warm-up of section 4.1, reading R21), fp64, causal prefill over L tokens.
+
+    For query t over keys s <= t: the target p_t is attention_target_row, the
+    indexer distribution is q_t = softmax_s(I[t,s]) with I = ReLU(u),
+    u[t,s] = (q_idx[t] W) . k_idx[s] on real-valued index vectors, and the
+    loss is sum_t KL(p_t || q_t) = sum_t sum_s p (log p - log q) (0 log 0 = 0).
+    Its gradient with respect to I[t,s] is q_t[s] - p_t[s]; through the ReLU
+    it is kept where u > 0.  With G that gradient and qf = q_idx W:
+      d qf = G k_idx;  d k_idx = G^T qf;  d q_idx = (d qf) W^T;  d W = q_idx^T (d qf).
+    `rows` restricts the queries whose terms are summed.  Returns
+    (loss, per-query losses [L], dq_idx [L,128], dk_idx [L,128], dW [128,128]).
+    """
+    qi = as_f64(q_idx)
+    ki = as_f64(k_idx)
+    wd = as_f64(w)
+    qa = q   # rows are read one at a time (q may be a row accessor)
+    kva = as_f64(kv)
+    L = qi.shape[0]
+    qf = fold(qi, wd)
+    losses = np.zeros(L)
+    dqf = np.zeros_like(qf)
+    dk = np.zeros_like(ki)
+    for t in (range(L) if rows is None else rows):
+        u = ki[: t + 1] @ qf[t]
+        i_row = relu(u)
+        m = np.max(i_row)
+        logq = i_row - (m + np.log(np.sum(np.exp(i_row - m))))
+        p = attention_target_row(as_f64(qa[t]), kva[: t + 1, :Dk], scale)
+        nz = p > 0
+        losses[t] = float(np.sum(p[nz] * (np.log(p[nz]) - logq[nz])))
+        g = (np.exp(logq) - p) * (u > 0)
+        dqf[t] = g @ ki[: t + 1]
+        dk[: t + 1] += np.outer(g, qf[t])
+    return float(np.sum(losses)), losses, dqf @ wd.T, dk, qi.T @ dqf
+
+
 # ---------------------------------------------------------- whole forward ---
 
 class PrefillOracle:

@@ -487,6 +487,59 @@ def pin_sparse_attn_backward_scatter(od, oc):
     assert np.all(dq[3] == 0)   # a query with no selected key
 
 
+def _kl_inputs(rng, L, H, Dk):
+    return (rng.standard_normal((L, 128)) * 0.3, rng.standard_normal((L, 128)) * 0.3,
+            rng.standard_normal((128, 128)) / np.sqrt(128), rng.standard_normal((L, H, Dk)),
+            rng.standard_normal((L, Dk + 4)))
+
+
+def pin_indexer_kl_autograd(od, oc):
+    """KL alignment loss and gradients against torch autograd of an
+    independently written fp64 loss (torch's log_softmax, relu and kl_div)."""
+    rng = np.random.default_rng(31)
+    for L, H, Dk in ((7, 3, 8), (12, 2, 16)):
+        qi, ki, w, q, kv = _kl_inputs(rng, L, H, Dk)
+        scale = 0.3
+        loss, losses, dqi, dki, dw = od.indexer_kl(qi, ki, w, q, kv, scale, Dk)
+        tq, tk, tw = (torch.tensor(a, requires_grad=True) for a in (qi, ki, w))
+        tot = 0
+        for t in range(L):
+            logits = torch.relu(tk[: t + 1] @ (tq[t] @ tw))
+            att = torch.softmax(scale * torch.tensor(q[t]) @ torch.tensor(kv[: t + 1, :Dk]).T, dim=1).mean(0)
+            lt = torch.nn.functional.kl_div(torch.log_softmax(logits, 0), att, reduction="sum")
+            assert abs(float(lt) - losses[t]) <= 1e-12 * (1 + abs(losses[t])), t
+            assert losses[t] >= -1e-15
+            tot = tot + lt
+        tot.backward()
+        assert abs(float(tot) - loss) <= 1e-11
+        assert np.allclose(dqi, tq.grad.numpy(), rtol=1e-10, atol=1e-13)
+        assert np.allclose(dki, tk.grad.numpy(), rtol=1e-10, atol=1e-13)
+        assert np.allclose(dw, tw.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def pin_indexer_kl_differences(od, oc):
+    """Central differences of the oracle's own loss match its gradients, and
+    the first query (one key) has zero loss and zero gradient."""
+    rng = np.random.default_rng(37)
+    L, H, Dk = 9, 2, 8
+    qi, ki, w, q, kv = _kl_inputs(rng, L, H, Dk)
+    scale = 0.5
+    loss, losses, dqi, dki, dw = od.indexer_kl(qi, ki, w, q, kv, scale, Dk)
+    assert losses[0] == 0.0
+    h = 1e-6
+    for arr, grad in ((qi, dqi), (ki, dki), (w, dw)):
+        for _ in range(4):
+            i = tuple(rng.integers(0, d) for d in arr.shape)
+            a0 = arr[i]
+            arr[i] = a0 + h
+            lp = od.indexer_kl(qi, ki, w, q, kv, scale, Dk)[0]
+            arr[i] = a0 - h
+            lm = od.indexer_kl(qi, ki, w, q, kv, scale, Dk)[0]
+            arr[i] = a0
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[i]) <= 1e-6 * (1 + abs(fd)), (i, fd, grad[i])
+
+
 def pin_page_constants(od, oc):
     """The write-up's constants and its ~3% indexer share at L=128K, checked
     against the 128K workload's shapes (a shape pin, not a parity pin)."""
@@ -513,4 +566,5 @@ ALL_PINS = [
     pin_scores_causal_relu, pin_topk_properties, pin_dynamic_k,
     pin_attend_special_cases, pin_sparse_equals_dense, pin_decode_equals_prefill_row, pin_page_constants,
     pin_attend_backward_autograd_and_differences, pin_sparse_attn_backward_scatter,
+    pin_indexer_kl_autograd, pin_indexer_kl_differences,
 ]

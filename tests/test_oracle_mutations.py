@@ -184,7 +184,19 @@ def _sparse_bwd_no_dv(q, kv, idx, scale, Dv, d_out, rows=None):
             np.add.at(dkv, sel, dk)
     return dq, dkv
 
+def _target_unscaled(q_heads, k_rows, scale):
+    return _orig_target(q_heads, k_rows, 1.0)
+
+
+def _target_summed(q_heads, k_rows, scale):
+    return _orig_target(q_heads, k_rows, scale) * np.asarray(q_heads).shape[0]
+
+
+_orig_target = od.attention_target_row
+
 MUTATIONS = {
+    "kl_target_unscaled": (od, "attention_target_row", _target_unscaled),
+    "kl_target_summed_not_averaged": (od, "attention_target_row", _target_summed),
     "attn_bwd_dropped_rowsum": (od, "attend_backward", _bwd_no_rowsum),
     "attn_bwd_dq_unscaled": (od, "attend_backward", _bwd_dq_unscaled),
     "sparse_bwd_dropped_dv_scatter": (od, "sparse_attn_backward", _sparse_bwd_no_dv),
