@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 #define DSA_INDEX_DIM 128   /* index-key width, write-up section 2.2 */
 #define DSA_MAX_TOPK 4096
 
@@ -212,6 +212,33 @@ dsa_status_t dsa_sparse_attn_bwd(const void* q, int64_t T, int64_t H, int64_t Dk
                                  int64_t k, float scale, const void* out, const float* lse_in,
                                  const void* d_out, void* dq, float* dkv, int64_t ld_dkv, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/*
+ * KL alignment of the lightning indexer to the dense attention (write-up
+ * section 4.1, dense warm-up: the indexer alone learns to imitate the
+ * frozen model's attention distribution through a KL loss).  Causal prefill
+ * of L tokens; for query t over keys s <= t:
+ *   p_t[s]  = (1/H) sum_h softmax_s(scale q[t,h] . kv[s, :Dk])  (target)
+ *   I[t,s]  = ReLU((q_idx[t] W) . k_idx[s]),  log q_t = I - logsumexp_s I
+ *   loss[t] = sum_s p_t[s] (log p_t[s] - log q_t[s])            (0 log 0 = 0)
+ * and with G[t,s] = (q_t[s] - p_t[s]) [I[t,s] > 0], qf = q_idx W:
+ *   dq_idx = (G k_idx) W^T,  dk_idx = G^T qf,  dw = q_idx^T (G k_idx).
+ * Index vectors and W are real-valued fp32 here (training, no FP8); the
+ * attention operands are the model's bf16 tensors.  All outputs are written.
+ *
+ * q_idx, k_idx  device fp32 [L][128];  w device fp32 [128][128]
+ * q             device bf16 [L][H][Dk];  kv device bf16 [L][ld_kv]
+ * loss_out      device fp32 [L];  dq_idx, dk_idx device fp32 [L][128];
+ * dw            device fp32 [128][128]
+ * Supported: dtype = DSA_BF16, H = 128, Dk = 576, 1 <= L <= 65536
+ * (otherwise DSA_ERR_UNSUPPORTED).  Workspace:
+ * dsa_indexer_kl_workspace_size(L) bytes (it holds the L x L score matrix).
+ */
+size_t dsa_indexer_kl_workspace_size(int64_t L);
+dsa_status_t dsa_indexer_kl(const float* q_idx, const float* k_idx, const float* w, const void* q, int64_t H,
+                            int64_t Dk, dsa_dtype_t dtype, const void* kv, int64_t ld_kv, int64_t L, float scale,
+                            float* loss_out, float* dq_idx, float* dk_idx, float* dw, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /*
  * Whole forward: fold, scores, top-k and sparse attention.

@@ -25,12 +25,13 @@ DSA_FLAG_FORCE_FALLBACK = 4
 DSA_FLAG_DYNAMIC_K = 8
 INDEX_DIM = 128
 MAX_TOPK = 4096
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTED = [
     "dsa_abi_version", "dsa_status_str", "dsa_fold_index_query", "dsa_index_scores",
     "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_dynamic", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
-    "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd", "dsa_forward_workspace_size", "dsa_forward",
+    "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd", "dsa_indexer_kl_workspace_size", "dsa_indexer_kl",
+    "dsa_forward_workspace_size", "dsa_forward",
 ]
 
 
@@ -75,6 +76,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "dsa_sparse_attn_bwd_workspace_size": ([c_i64, c_i64, c_i64], c_sz),
         "dsa_sparse_attn_bwd": ([c_vp, c_i64, c_i64, c_i64, c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_f,
                                  c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_sz, c_vp], c_int),
+        "dsa_indexer_kl_workspace_size": ([c_i64], c_sz),
+        "dsa_indexer_kl": ([c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_vp, c_i64, c_i64, c_f, c_vp, c_vp, c_vp,
+                            c_vp, c_vp, c_sz, c_vp], c_int),
         "dsa_forward_workspace_size": ([ctypes.POINTER(ForwardArgs)], c_sz),
         "dsa_forward": ([ctypes.POINTER(ForwardArgs), c_vp, c_vp, c_vp, c_sz, c_vp], c_int),
     }
@@ -210,6 +214,23 @@ def dsa_sparse_attn_bwd(q, kv, idx, scale, out, lse, d_out, Dv, dq=None, dkv=Non
         _p(q), T, H, Dk, _dtype_code(q), _p(kv), kv.stride(0), Dv, S, _p(idx), k, ctypes.c_float(scale), _p(out),
         _p(lse), _p(d_out), _p(dq), _p(dkv), dkv.stride(0), _p(ws), ws.numel(), _stream(stream)))
     return dq, dkv
+
+
+def dsa_indexer_kl(q_idx, k_idx, w, q, kv, scale, stream=None):
+    """Per-query KL losses and the gradients (dq_idx, dk_idx, dw) of the
+    indexer alignment; all fp32 except the bf16 attention operands."""
+    L, H, Dk = q.shape
+    dev = q.device
+    loss = torch.empty(L, dtype=torch.float32, device=dev)
+    dq_idx = torch.empty((L, 128), dtype=torch.float32, device=dev)
+    dk_idx = torch.empty((L, 128), dtype=torch.float32, device=dev)
+    dw = torch.empty((128, 128), dtype=torch.float32, device=dev)
+    wsb = lib().dsa_indexer_kl_workspace_size(L)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _check("dsa_indexer_kl", lib().dsa_indexer_kl(
+        _p(q_idx), _p(k_idx), _p(w), _p(q), H, Dk, _dtype_code(q), _p(kv), kv.stride(0), L, ctypes.c_float(scale),
+        _p(loss), _p(dq_idx), _p(dk_idx), _p(dw), _p(ws), ws.numel(), _stream(stream)))
+    return loss, dq_idx, dk_idx, dw
 
 
 def forward_args(x: dict, topk: int, scale: float, Dv: int, mode: int = DSA_MODE_PREFILL, flags: int = 0,

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["fold.hip", "index_scores.hip", "topk.hip", "index_select.hip", "attn.hip", "attn_bwd.hip", "api.cpp"]
+SOURCES = ["fold.hip", "index_scores.hip", "topk.hip", "index_select.hip", "attn.hip", "attn_bwd.hip", "indexer_kl.hip", "api.cpp"]
 SOURCE_FLAGS = {}   # per-source extra hipcc flags
 ARCH = "gfx950"
 FLAGS = [

@@ -339,6 +339,46 @@ dsa_status_t dsa_sparse_attn_bwd(const void* q, int64_t T, int64_t H, int64_t Dk
   }
 }
 
+size_t dsa_indexer_kl_workspace_size(int64_t L) {
+  if (L < 1 || L > 65536) return 0;
+  return indexer_kl_workspace_bytes(L);
+}
+
+dsa_status_t dsa_indexer_kl(const float* q_idx, const float* k_idx, const float* w, const void* q, int64_t H,
+                            int64_t Dk, dsa_dtype_t dtype, const void* kv, int64_t ld_kv, int64_t L, float scale,
+                            float* loss_out, float* dq_idx, float* dk_idx, float* dw, void* ws, size_t ws_bytes,
+                            void* stream) {
+  try {
+    if (L < 0 || ld_kv < Dk) return DSA_ERR_SHAPE;
+    if (dtype != DSA_BF16) return dtype == DSA_F32 ? DSA_ERR_UNSUPPORTED : DSA_ERR_DTYPE;
+    if (L == 0) return DSA_OK;
+    if (!indexer_kl_supported(H, Dk, L)) return DSA_ERR_UNSUPPORTED;
+    if (!q_idx || !k_idx || !w || !q || !kv || !loss_out || !dq_idx || !dk_idx || !dw) return DSA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(kv, 16) || (ld_kv * 2) % 16 || !aligned(k_idx, 16) || !aligned(dq_idx, 16) ||
+        !aligned(dk_idx, 16))
+      return DSA_ERR_SHAPE;
+    const size_t need = indexer_kl_workspace_bytes(L);
+    if (ws_bytes < need || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
+    DSA_TRY(check_device());
+    KlArgs a{};
+    a.q_idx = q_idx;
+    a.k_idx = k_idx;
+    a.w = w;
+    a.q = q;
+    a.kv = kv;
+    a.ld_kv = ld_kv;
+    a.L = L;
+    a.scale = scale;
+    a.loss = loss_out;
+    a.dq_idx = dq_idx;
+    a.dk_idx = dk_idx;
+    a.dw = dw;
+    return from_hip(launch_indexer_kl(a, ws, as_stream(stream)));
+  } catch (...) {
+    return DSA_ERR_DEVICE;
+  }
+}
+
 size_t dsa_forward_workspace_size(const dsa_forward_args* a) {
   if (!a || check_forward(a) != DSA_OK) return 0;
   const FwdPlan p = plan_forward(a, true);

@@ -77,6 +77,24 @@ int64_t attn_bwd_chunk(int64_t T, int64_t k);
 size_t attn_bwd_workspace_bytes(int64_t T, int64_t k);
 hipError_t launch_attn_bwd(const BwdArgs& a, void* ws, hipStream_t st);
 
+// indexer_kl.hip: KL alignment of the indexer to the dense attention
+struct KlArgs {
+  const float* q_idx;   // [L][128] fp32
+  const float* k_idx;   // [L][128] fp32
+  const float* w;       // [128][128] fp32
+  const void* q;        // [L][128][576] bf16
+  const void* kv;       // [L][ld_kv] bf16
+  int64_t ld_kv, L;
+  float scale;
+  float* loss;          // [L]
+  float* dq_idx;        // [L][128]
+  float* dk_idx;        // [L][128]
+  float* dw;            // [128][128]
+};
+bool indexer_kl_supported(int64_t H, int64_t Dk, int64_t L);
+size_t indexer_kl_workspace_bytes(int64_t L);
+hipError_t launch_indexer_kl(const KlArgs& a, void* ws, hipStream_t st);
+
 // attn.hip
 struct AttnArgs {
   const void* q;        // [T][H][Dk]

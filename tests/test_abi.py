@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 4
+    assert lib.dsa_abi_version() == 5
     for s in range(7):
         assert lib.dsa_status_str(s)
     assert lib.dsa_status_str(99) == b"unknown status"
@@ -111,6 +111,26 @@ def test_attn_bwd_validation(lib):
     assert call(wsb=16) == 5
     assert call(T=0) == 0
     assert lib.dsa_sparse_attn_bwd_workspace_size(4, 128, 64) > 0
+
+
+def test_indexer_kl_validation(lib):
+    f = lib.dsa_indexer_kl
+    p = _vp(0x100000)
+    sc = ctypes.c_float(0.04)
+    args = dict(qi=p, ki=p, w=p, q=p, H=128, Dk=576, dt=B.DSA_BF16, kv=p, ldkv=576, L=64, sc=sc, loss=p, dqi=p,
+                dki=p, dw=p, ws=p, wsb=1 << 30, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+    assert call(dt=B.DSA_F32) == 4
+    assert call(H=16) == 4
+    assert call(L=1 << 17) == 4
+    assert call(ldkv=100) == 2
+    assert call(dw=None) == 1
+    assert call(wsb=16) == 5
+    assert call(L=0) == 0
+    assert lib.dsa_indexer_kl_workspace_size(64) >= 64 * 64 * 4
 
 
 def test_attn_validation(lib):
