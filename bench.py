@@ -209,6 +209,43 @@ def backward_stats(B, torch, spec, x, idx, out, pairs, reps=3):
                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}}
 
 
+def bench_kl(args, B, gen, torch, dev):
+    """The indexer's KL alignment step (dense warm-up) on an L-token
+    MLA-shaped prefill with fp32 index vectors: HIP events around whole
+    dsa_indexer_kl calls on the launch stream."""
+    L = args.kl
+    spec = gen.PREFILL_32K.with_(name=f"kl_L{L}", L=L, fp8=False)
+    log("KL alignment, L =", L)
+    x = gen.make_prefill(spec, seed=0, device=dev)
+    B.dsa_indexer_kl(x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], spec.scale)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        B.dsa_indexer_kl(x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], spec.scale)
+    ev0.record(st)
+    for _ in range(args.steps):
+        loss = B.dsa_indexer_kl(x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"], spec.scale)[0]
+    ev1.record(st)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    pairs = L * (L + 1) // 2
+    flops_target = 2 * 2.0 * spec.H * spec.Dk * pairs     # two passes of q . k over the heads
+    flops = flops_target + 3 * 2.0 * 128 * pairs         # index scores, G k, G^T qf
+    achieved = flops / (ms * 1e-3) / 1e12
+    log(f"KL step {ms:.2f} ms = {achieved:.1f} TFLOP/s")
+    print(json.dumps({
+        "metric": "indexer KL alignment step (loss + gradients), causal L-token prefill",
+        "value": round(L / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "dtype_detail": "attention target bf16 MFMA; indexer and gradients fp32",
+        "data": "synthetic", "config": {"workload": spec.name, "L": L, "heads": spec.H, "dk": spec.Dk},
+        "total_loss": float(loss.sum()),
+        "roofline": {"bound": "mfma", "kernel": "kl_target_kernel<576>", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "algorithmic_flops": flops, "note": "whole step over its dominant FLOPs"}}), flush=True)
+
+
 def bench_long(args, B, gen, torch, dev):
     """The 2^20-token prefill as chunks of C queries (each chunk attends over
     the keys of every earlier chunk and its own), then a 64-sequence decode
@@ -312,6 +349,8 @@ def main():
     ap.add_argument("--dynamic-theta", type=float, default=None,
                     help="per-query k: keep the keys scoring above this (within [--dynamic-kmin, k])")
     ap.add_argument("--dynamic-kmin", type=int, default=0)
+    ap.add_argument("--kl", type=int, default=0, metavar="L",
+                    help="time only the indexer KL alignment step (loss and gradients) on an L-token MLA prefill")
     ap.add_argument("--backward", action="store_true",
                     help="also time the sparse attention backward (dq, dkv) over the prefill's selection")
     ap.add_argument("--profile-attn", type=int, default=0, metavar="N",
@@ -329,6 +368,9 @@ def main():
 
     B.lib()
     dev = torch.device("cuda:0")
+    if args.kl:
+        bench_kl(args, B, gen, torch, dev)
+        return
     if args.workload == gen.PREFILL_1M.name:
         bench_long(args, B, gen, torch, dev)
         return
