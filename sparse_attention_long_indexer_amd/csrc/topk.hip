@@ -62,6 +62,7 @@ constexpr int kCandCap = 8192;          // candidates a row may stage in LDS
 constexpr int kCandWin = 64;            // sampled keys per window (one wave)
 constexpr int kCandWins = 64;           // windows per row (at least), one per stratum
 constexpr int kCandWinsMax = 4096;      // ... and at most
+constexpr int kCandSampleLds = 8192;    // samples staged in LDS (rows up to 2^18 keys)
 constexpr int kCandSpan = 4096;         // keys per filter block
 constexpr int kCandThreads = 512;
 constexpr int kCandWaves = kCandThreads / 64;
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRo
                                                                          uint32_t* __restrict__ tau,
                                                                          int32_t* __restrict__ cnt) {
   __shared__ uint32_t wstart[kCandWinsMax];
+  __shared__ uint32_t skey[kCandSampleLds];
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t scan[kCandWaves];
   __shared__ uint32_t s_out[2];
@@ -121,12 +123,35 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRo
     wstart[wi] = (uint32_t)(s0 + (int64_t)(mix32((uint32_t)(row * kCandWinsMax + wi) ^ 0x9e3779b9u) % slots));
   }
   __syncthreads();
+  // samples of rows up to 2^18 keys are staged in LDS for the select's
+  // passes; longer rows' samples are read again from the score row
   auto key_at = [&](int64_t i) { return score_key(rv.p[wstart[i >> 6] + (i & (kCandWin - 1))]); };
+  const bool staged = nsamp <= kCandSampleLds;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int64_t i = tid; i < nsamp; i += kCandThreads) {
-    const uint32_t key = key_at(i);
-    mn = min(mn, key);
-    mx = max(mx, key);
+  if (staged) {  // every load issued before the first use
+    constexpr int PER = kCandSampleLds / kCandThreads;
+    float v[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = tid + r * kCandThreads;
+      v[r] = i < nsamp ? rv.p[wstart[i >> 6] + (i & (kCandWin - 1))] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = tid + r * kCandThreads;
+      if (i < nsamp) {
+        const uint32_t key = score_key(v[r]);
+        skey[i] = key;
+        mn = min(mn, key);
+        mx = max(mx, key);
+      }
+    }
+  } else {
+    for (int64_t i = tid; i < nsamp; i += kCandThreads) {
+      const uint32_t key = key_at(i);
+      mn = min(mn, key);
+      mx = max(mx, key);
+    }
   }
   mn = wave_min(mn);
   mx = wave_max(mx);
@@ -144,7 +169,11 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRo
   }
   __syncthreads();
   uint32_t thr, need;
-  radix_select<kCandThreads>(key_at, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr, need);
+  if (staged)
+    radix_select<kCandThreads>([&](int64_t i) { return skey[i]; }, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr,
+                               need);
+  else
+    radix_select<kCandThreads>(key_at, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr, need);
   if (tid == 0) tau[row] = thr == kZeroKey ? kZeroKey + 1 : thr;
 }
 
