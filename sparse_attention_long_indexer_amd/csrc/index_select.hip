@@ -632,7 +632,7 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   const bool ok = bucketed ? output_bucketed_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel,
                                                                         s_tie, kMaxTies, &s_ntie, wave_cnt, o)
                           : output_from_candidates<kSelThreads>(cl, nslots, thr, need, n, m, topk, sel, nwords,
-                                                                s_tie, kMaxTies, &s_ntie, wave_cnt, o);
+                                                                s_tie, kMaxTies, &s_ntie, wave_cnt, o, hist);
   if (!ok) {
     if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
   }

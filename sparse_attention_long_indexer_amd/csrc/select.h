@@ -220,14 +220,22 @@ __device__ inline int64_t select_row(const float* __restrict__ p, int64_t n, int
 // whose key equals thr, and write the m kept positions in ascending order to
 // o[0 .. m), padding o[m .. topk) with -1.  Kept positions are marked in a
 // bitmap of nwords words (zeroed by the caller, as is *s_ntie); keys equal
-// to thr go through the tie list `tie` (max_ties entries).  Positions outside
-// [0, n) are skipped (invalid slots).  Returns false, with nothing written
-// to o, when the tie list overflows; the caller settles the row elsewhere.
+// to thr go through the tie list `tie` (max_ties entries).  When the list
+// overflows (typically ReLU's zeros at the boundary of a short row) and the
+// row has at most 32 * kTieBitmapWords positions, the ties are marked in a
+// second bitmap `tie_bits` (LDS scratch of kTieBitmapWords words, may be
+// null) and the `need` lowest are found by prefix popcounts.  Positions
+// outside [0, n) are skipped (invalid slots).  Returns false, with nothing
+// written to o, when the ties cannot be settled; the caller settles the row
+// elsewhere.
+constexpr int kTieBitmapWords = 1024;
+
 template <int NT>
 __device__ inline bool output_from_candidates(const uint2* cl, int nslots, uint32_t thr, uint32_t need,
                                               int64_t n, int64_t m, int64_t topk, uint32_t* bitmap,
                                               int nwords, int32_t* tie, int max_ties, int* s_ntie,
-                                              uint32_t* wave_cnt, int32_t* __restrict__ o) {
+                                              uint32_t* wave_cnt, int32_t* __restrict__ o,
+                                              uint32_t* tie_bits = nullptr) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int e = tid; e < nslots; e += NT) {
@@ -244,12 +252,50 @@ __device__ inline bool output_from_candidates(const uint2* cl, int nslots, uint3
   }
   __syncthreads();
   const int ntie = *s_ntie;
-  if (ntie > max_ties) return false;
-  for (int i = tid; i < ntie; i += NT) {
-    const int32_t p = tie[i];
-    int rank = 0;
-    for (int j = 0; j < ntie; ++j) rank += tie[j] < p ? 1 : 0;
-    if (rank < (int)need) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+  if (ntie > max_ties) {
+    if (!tie_bits || nwords > kTieBitmapWords) return false;
+    for (int i = tid; i < nwords; i += NT) tie_bits[i] = 0u;
+    __syncthreads();
+    for (int e = tid; e < nslots; e += NT) {
+      const uint2 cv = cl[e];
+      const int32_t p = (int32_t)cv.y;
+      if (cv.x == thr && p >= 0 && p < n) atomicOr(&tie_bits[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    // the `need` lowest tie positions: exclusive prefix of the popcounts over
+    // runs of `per` words per thread, then each thread walks its run
+    const int per = (nwords + NT - 1) / NT;
+    const int w0 = tid * per, w1 = min(nwords, w0 + per);
+    uint32_t mine = 0;
+    for (int i = w0; i < w1; ++i) mine += __popc(tie_bits[i]);
+    uint32_t incl = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_cnt[w] = incl;
+    __syncthreads();
+    uint32_t rank = incl - mine;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) rank += (i < w) ? wave_cnt[i] : 0u;
+    for (int i = w0; i < w1 && rank < need; ++i) {
+      uint32_t wv = tie_bits[i], keep = 0u;
+      while (wv && rank < need) {
+        const uint32_t b = wv & (0u - wv);
+        keep |= b;
+        ++rank;
+        wv ^= b;
+      }
+      if (keep) atomicOr(&bitmap[i], keep);
+    }
+    __syncthreads();  // wave_cnt is reused below
+  } else {
+    for (int i = tid; i < ntie; i += NT) {
+      const int32_t p = tie[i];
+      int rank = 0;
+      for (int j = 0; j < ntie; ++j) rank += tie[j] < p ? 1 : 0;
+      if (rank < (int)need) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+    }
   }
   __syncthreads();
   // prefix popcount over the bitmap: thread tid owns a run of `per` words

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_cand_select_kernel(TopkRows
   const bool ok = bucketed ? output_bucketed_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, s_tie, kCandMaxTies,
                                                                &s_ntie, sh.wave_cnt, o)
                           : output_from_candidates<NT>(cl, c, thr, need, n, m, k, bitmap, nwords, s_tie,
-                                                       kCandMaxTies, &s_ntie, sh.wave_cnt, o);
+                                                       kCandMaxTies, &s_ntie, sh.wave_cnt, o, sh.hist);
   if (!ok) {
     __syncthreads();
     m = select_row(rv.p, n, k, o, sh, dyn);  // a boundary tie too long for the list
