@@ -144,6 +144,7 @@ ATTN_CASES = [
     ("bf16_h16_d128", gen.PREFILL_8K.with_(L=3000), 2048),
     ("bf16_mla", gen.PREFILL_32K.with_(L=2500), 2048),
     ("bf16_mla_unit", gen.PREFILL_32K.with_(L=2500, qkv_unit=True), 700),
+    ("bf16_mla_k4096", gen.PREFILL_32K.with_(L=5000), 4096),      # the largest k
 ]
 
 
@@ -227,6 +228,45 @@ def test_forward_prefill(dev, spec):
             worst = max(worst, P.check_attn(g, o, f32=spec.attn_f32))
     say(f"rows={len(rows)} window-diffs={diffs} worst-attn={worst:.3g}")
     assert diffs <= max(2, len(rows) // 10)
+
+
+@pytest.mark.parametrize("flags", [0, B.DSA_FLAG_FUSED], ids=["default", "fused"])
+def test_forward_k_at_least_L_is_dense(dev, flags):
+    """With k >= L every query keeps all of its causal keys, so the sparse
+    forward is dense causal attention (the write-up's sparse attention
+    reduces to ordinary attention when nothing is dropped)."""
+    spec = gen.PREFILL_32K.with_(name="dense_L300", L=300, topk=512)
+    x = gen.make_prefill(spec, seed=13, device=dev)
+    out, idx = run_forward(spec, x, dev, flags)
+    gi = idx.cpu().numpy()
+    for t in range(spec.L):
+        assert np.array_equal(gi[t, : t + 1], np.arange(t + 1)) and np.all(gi[t, t + 1:] == -1), t
+    kv = od.as_f64(to_np(x["kv"]))
+    q = to_np(x["q"])
+    for t in (0, 1, 17, 150, 299):
+        o, _ = od.attend(od.as_f64(q[t]), kv[: t + 1], kv[: t + 1, : spec.Dv], spec.scale)
+        P.check_attn(od.as_f64(to_np(out[t])), o)
+
+
+def test_forward_single_token(dev):
+    """L = 1: the only query attends to its own key with weight 1, so the
+    output is its value row (bf16, exact)."""
+    spec = gen.PREFILL_32K.with_(name="single", L=1, topk=1)
+    x = gen.make_prefill(spec, seed=14, device=dev)
+    out, idx = run_forward(spec, x, dev)
+    assert idx.cpu().tolist() == [[0]]
+    want = x["kv"][0, : spec.Dv].float().expand(spec.H, spec.Dv)
+    assert torch.equal(out[0].float(), want)
+
+
+def test_forward_empty(dev):
+    """T = 0 is a no-op through the whole forward."""
+    spec = gen.PREFILL_32K.with_(name="empty", L=0, topk=64)
+    x = gen.make_prefill(spec, seed=15, device=dev)
+    out = torch.empty((0, spec.H, spec.Dv), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((0, spec.topk), dtype=torch.int32, device=dev)
+    B.dsa_forward(B.forward_args(x, spec.topk, spec.scale, spec.Dv), out, idx_out=idx)
+    torch.cuda.synchronize()
 
 
 def test_forward_deterministic(dev):
