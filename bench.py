@@ -357,8 +357,8 @@ def main():
                     help="only run the counter-profile sequence (a 2 GiB copy, then N attention launches)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the prefill shards by query rows, decode by sequence; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(a prefill would shard by query rows, a decode batch by sequence).", file=sys.stderr)
         sys.exit(2)
 
     import torch
