@@ -317,7 +317,7 @@ def bench_long(args, B, gen, torch, dev):
         "config": {"workload": spec.name, "L": L, "chunk": C, "topk": k, "heads": spec.H, "dk": spec.Dk,
                    "dv": spec.Dv, "batch": 1, "index_dim": 128},
         "chunk_ms": chunk_ms,
-        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<576,512,8>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_mla_kernel", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "ms_per_launch": round(attn_ms, 3), "algorithmic_flops_per_launch": flops,
                      "note": "last chunk: the chunk's queries over all 2^20 keys"},
@@ -421,8 +421,8 @@ def main():
         flops = 2.0 * spec.H * (spec.Dk + spec.Dv) * pairs
     achieved = flops / (attn_ms * 1e-3) / 1e12
     sha = kernel_source_sha(["attn.hip", "common.h", "kernels.h"])
-    traffic = load_traffic("attn_bf16_kernel<576,512,8>", sha)
-    roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<576,512,8>", "achieved": round(achieved, 2),
+    traffic = load_traffic("attn_mla_kernel", sha)
+    roof = {"bound": "mfma", "kernel": "attn_mla_kernel", "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic, "ms_per_launch": round(attn_ms, 3),
             "algorithmic_flops_per_launch": flops, "selected_pairs": pairs}

@@ -3,15 +3,17 @@
 // selected keys, all query heads sharing one key/value head as in MLA's MQA
 // mode).
 //
-// bf16 path: one block per query (or per key split of one), 16 heads per
-// wave.  Per tile of 32 selected keys the block gathers the rows into LDS
-// with direct-to-LDS copies (double buffered: the gather of tile i+1 runs
-// during tile i), then
+// Two bf16 kernels.  The MLA shape with the shared latent row (128 heads,
+// key = 576-wide latent row, value = its first 512 columns) runs
+// attn_mla_kernel, where two groups of four waves alternate between S^T +
+// softmax and PV so that each SIMD always has one wave feeding its matrix
+// core (described at the kernel).  The other shapes (16 heads of 128, and
+// MLA with a separate value tensor) run attn_bf16_kernel: one block per
+// query (or per key split of one), 16 heads per wave.  Per tile of 32
+// selected keys the block gathers the rows into LDS with direct-to-LDS
+// copies (double buffered: the gather of tile i+1 runs during tile i), then
 //   S^T = K . Q^T   with v_mfma_f32_16x16x32_bf16 (A = K fragments from LDS,
-//                   B = Q^T held in registers for the whole loop); for the
-//                   MLA shape, waves w and w^1 split the 576 key dims and
-//                   swap partial sums, so each K fragment read feeds two
-//                   MFMAs,
+//                   B = Q^T held in registers for the whole loop),
 //   an online softmax per head in the log2 domain, P^T to LDS, and
 //   O^T += V^T . P^T per wave for all heads over its own slice of the value
 //                   columns (A = V^T via transposed LDS reads, B = P^T).
@@ -121,10 +123,6 @@ __device__ __forceinline__ void lds_read_vt4(const char* lds_ptr, v8s* av) {
   }
 }
 
-// split QK over the key dims between wave pairs (shared-latent shapes with
-// an even number of waves)
-constexpr bool attn_ksplit(int DK, int NW, bool SEPV) { return !SEPV && NW % 2 == 0 && (DK / 32) % 2 == 0; }
-
 template <int DK, int DV, int NW, bool SEPV>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const int64_t* seq_off) {
   constexpr int NK = 32;                        // keys per tile
@@ -143,20 +141,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   constexpr int NFRAG = KF + 2 * (VC / 4);      // fragments per tile
   constexpr int LOADS = (NFRAG + NW - 1) / NW;  // fragment copies per wave per tile
   constexpr int VF = VCH / 4;
-  // QK split over the key dimension: waves w and w^1 both compute S^T for
-  // heads 16w .. 16w+15 and 16(w^1) .. 16(w^1)+15, wave w over half w%2 of
-  // the Dk dims, so each K fragment read from LDS feeds two MFMAs; the pair
-  // then swaps partial sums through LDS and wave w keeps heads 16w .. 16w+15
-  // for the softmax
-  constexpr bool KSPLIT = attn_ksplit(DK, NW, SEPV);
-  constexpr int KKW = KSPLIT ? DK / 64 : DK / 32;  // k-steps of 32 dims per wave
-  constexpr int HSW = KSPLIT ? 2 : 1;              // 16-head subtiles per wave in QK
-  // dynamic LDS: [2][TILE_BYTES] tiles | [NW] P^T fragments (1 KB) |
-  // KSPLIT: [NW][2] partial S^T fragments (1 KB) | index row
+  constexpr int KKW = DK / 32;  // k-steps of 32 dims
+  // dynamic LDS: [2][TILE_BYTES] tiles | [NW] P^T fragments (1 KB) | index row
   extern __shared__ __align__(16) char smem[];
   char* pbuf = smem + 2 * TILE_BYTES;
-  char* xbuf = pbuf + NW * 1024;
-  int32_t* sidx = (int32_t*)(xbuf + (KSPLIT ? NW * 2048 : 0));
+  int32_t* sidx = (int32_t*)(pbuf + NW * 1024);
   __shared__ float s_corr[H], s_l[H];
   __shared__ int s_need[NW];
   __shared__ int s_cnt;
@@ -218,17 +207,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     }
   };
 
-  // Q^T fragments, dims 32(kk0 + kk) + 8g .. +8, of head 16w + c (subtile
-  // HSW-1, kept) and, when split, of the partner's head 16(w^1) + c
-  // (subtile 0, handed over)
-  const int kk0 = KSPLIT ? (w & 1) * KKW : 0;
-  v8s qf[HSW][KKW];
+  // Q^T fragments, dims 32kk + 8g .. +8, of head 16w + c
+  v8s qf[KKW];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((t * H) + 16 * w + c) * (int64_t)DK + 8 * g;
 #pragma unroll
-  for (int hs = 0; hs < HSW; ++hs) {
-    const int hq = (hs == HSW - 1 ? 16 * w : 16 * (w ^ 1)) + c;
-    const uint16_t* qp = (const uint16_t*)a.q + ((t * H) + hq) * (int64_t)DK + 8 * g + 32 * kk0;
-#pragma unroll
-    for (int kk = 0; kk < KKW; ++kk) qf[hs][kk] = *(const v8s*)(qp + 32 * kk);
+    for (int kk = 0; kk < KKW; ++kk) qf[kk] = *(const v8s*)(qp + 32 * kk);
   }
   // O^T accumulators: value subtile d of this wave's columns x head subtile hs
   v4f o[ND][NW];
@@ -262,34 +246,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     const char* tb = smem + (it & 1) * TILE_BYTES;
     const int j0 = it * NK;
     // S^T = K . Q^T (key subtiles ks = rows 16ks + c)
-    v4f sacc[2][HSW];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int hs = 0; hs < HSW; ++hs) sacc[ks][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
+    v4f sc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kk = 0; kk < KKW; ++kk) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const v8s kf = *(const v8s*)(tb + ((ks * (KC / 4) + kk0 + kk) * 64 + kslot) * 16);
-#pragma unroll
-        for (int hs = 0; hs < HSW; ++hs) sacc[ks][hs] = mfma_bf16_16x16x32(kf, qf[hs][kk], sacc[ks][hs]);
+        const v8s kf = *(const v8s*)(tb + ((ks * (KC / 4) + kk) * 64 + kslot) * 16);
+        sc[ks] = mfma_bf16_16x16x32(kf, qf[kk], sc[ks]);
       }
       if (kk % DSA_QK_GROUP == DSA_QK_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    v4f sc[2];
-    if constexpr (KSPLIT) {
-      // hand the partner wave its heads' partial sums, add the partner's
-      // half to ours
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) *(v4f*)(xbuf + ((w * 2 + ks) * 64 + lane) * 16) = sacc[ks][0];
-      lds_barrier();
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        sc[ks] = sacc[ks][HSW - 1] + *(const v4f*)(xbuf + (((w ^ 1) * 2 + ks) * 64 + lane) * 16);
-    } else {
-      sc[0] = sacc[0][0];
-      sc[1] = sacc[1][0];
     }
     // online softmax (log2 domain); the running max only moves when a tile
     // raises it by more than 2^8, so O is rescaled rarely
@@ -394,6 +359,265 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
       const float l = s_l[h];
       const float inv = l > 0.f ? 1.f / l : 0.f;
       uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV + DVW * w;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        v2i pk;
+        pk[0] = (int)pack_bf16x2(o[d][hs][0] * inv, o[d][hs][1] * inv);
+        pk[1] = (int)pack_bf16x2(o[d][hs][2] * inv, o[d][hs][3] * inv);
+        *(v2i*)(op + 16 * d + 4 * g) = pk;
+      }
+    }
+  }
+}
+
+// ---- MLA shape, shared latent row: two wave groups in ping-pong -----------
+// 128 heads, key = the 576-wide latent row, value = its first 512 columns.
+// Eight waves, two per SIMD (wave w runs on SIMD w % 4), in two groups
+// G = w / 4.  Wave w computes S^T and the softmax for heads 16w .. 16w+15
+// over all 576 key dims, and accumulates O^T for all 128 heads over value
+// columns 64w .. 64w+63.  The loop runs in slots closed by block barriers:
+// in slot 2j group 0 does S^T + softmax of tile j while group 1 does PV of
+// tile j-1, in slot 2j+1 group 1 does S^T + softmax of tile j while group 0
+// does PV of tile j-1.  Each SIMD then always holds one wave feeding its
+// matrix core while the other is in its softmax or waiting on LDS, and the
+// S^T wave runs at raised priority so its softmax starts early.  Tile j is
+// read in slots 2j .. 2j+3; group 1 gathers tile j+1 at the start of slot
+// 2j into the third buffer and awaits it at the end of slot 2j+1.  P^T and
+// the rescale factors are double buffered by tile parity.
+//
+// Tile layout (unswizzled): fragment (ks, q) holds chunks 4q .. 4q+3 of
+// rows 16ks .. 16ks+15, slot = 16 (X % 4) + row % 16, so lane l of an S^T
+// operand read takes 16 bytes at 16 l (the conflict-free ds_read_b128
+// pattern); the transposed V^T reads are then 2-way conflicted, but they
+// are an eighth of the LDS read traffic.
+constexpr int kMlaTile = 32 * (576 / 8) * 16;         // 32 latent rows, 36 KB
+constexpr size_t kMlaFixedLds = 3 * kMlaTile + 2 * 8 * 1024;
+
+#ifndef DSA_MLA_QKG
+#define DSA_MLA_QKG 3  // k-steps of S^T read per LDS round trip (2 fragments each)
+#endif
+
+// 2^x with the hardware instruction alone: results below 2^-126 flush to
+// zero, which for softmax weights relative to a running max (sum >= 1) is
+// far below the bf16 rounding of P
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int64_t* seq_off) {
+  constexpr int NK = 32, DK = 576, DV = 512, H = 128, NW = 8;
+  constexpr int VF = DK / 32;       // fragments (32 dims) per 16-key subtile
+  constexpr int KK = DK / 32;       // k-steps of S^T
+  constexpr int ND = DV / NW / 16;  // value subtiles per wave
+  extern __shared__ __align__(16) char smem[];
+  char* pbuf = smem + 3 * kMlaTile;                 // [parity][wave][lane] 16-byte P^T fragments
+  int32_t* sidx = (int32_t*)(pbuf + 2 * 8 * 1024);  // the block's index row
+  __shared__ float s_corr[2][H], s_l[H];
+  __shared__ int s_need[2][NW];
+  __shared__ int s_cnt;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int G = w >> 2, gw = w & 3;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t t = blockIdx.x / a.splits;
+  const int sp = (int)(blockIdx.x % a.splits);
+  const AttnRow row = attn_row(a, seq_off, t);
+  if (tid == 0) s_cnt = (int)a.k;
+  __syncthreads();
+  {
+    int first = (int)a.k;
+    for (int j = tid; j < (int)a.k; j += NW * 64) {
+      int32_t s = row.ip[j];
+      if (s < 0 && j < first) first = j;
+      sidx[j] = s < row.len ? s : (int32_t)(row.len - 1);
+    }
+    if (first < (int)a.k) atomicMin(&s_cnt, first);
+  }
+  __syncthreads();
+  const int nvalid = s_cnt;
+  const int per = ((nvalid + a.splits - 1) / a.splits + NK - 1) / NK * NK;
+  const int kbeg = min(nvalid, sp * per);
+  const int n = min(nvalid, kbeg + per);
+  const int ntiles = (n - kbeg + NK - 1) / NK;
+  const uint32_t ldk = (uint32_t)(a.ld_kv * 2);  // bytes; rows * ld * 2 < 4 GiB (checked by the launcher)
+  const char* kvq = (const char*)a.kv + row.base * (int64_t)ldk;
+
+  // gather (group 1): copy i of wave 4 + gw fills fragment f = 4i + gw;
+  // lane l brings chunk 4q + l/16 of row 16ks + l%16 to slot l
+  const uint32_t lofs = 16u * (uint32_t)(lane >> 4);
+  auto issue_tile = [&](int jl) {
+    const int j0 = kbeg + jl * NK;
+    char* dst = smem + (jl % 3) * kMlaTile;
+    const int ja = j0 + c, jb = j0 + 16 + c;
+    const uint32_t ra = (uint32_t)sidx[ja < n ? ja : j0], rb = (uint32_t)sidx[jb < n ? jb : j0];
+#pragma unroll
+    for (int i = 0; i < 2 * VF / 4; ++i) {
+      const int f = 4 * i + gw;
+      const int ks = f >= VF ? 1 : 0, q = f - VF * ks;
+      const char* src = kvq + 64 * q + ((ks ? rb : ra) * ldk + lofs);
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)((lds_char*)dst + f * 1024), 16, 0,
+                                       0);
+    }
+  };
+
+  // Q^T fragments of head 16w + c, dims 32kk + 8g .. +7
+  v8s qf[KK];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((t * H) + 16 * w + c) * (int64_t)DK + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v8s*)(qp + 32 * kk);
+  }
+  v4f o[ND][8];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int hs = 0; hs < 8; ++hs) o[d][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+  const float zs = a.scale * kLog2e;
+  // V^T reads: lane (sl, G') reads row 4G' + sl/4 (+16 for key subtile 1),
+  // value columns 16D + 4(sl%4) .. +3: chunk 2D + (sl%4)/2, half sl%2
+  const int vbase = ((((lane & 3) >> 1) * 16) + (4 * (lane >> 4) + ((lane & 15) >> 2))) * 16 + (lane & 1) * 8;
+
+  // S^T = K . Q^T for the wave's 16 heads (key subtiles 0 and 1, even and
+  // odd k-steps in separate accumulators), then the online softmax in the
+  // log2 domain; the running max only moves when a tile raises it by more
+  // than 2^8.  P^T, the rescale factors and the moved flag go to LDS.
+  auto qk_softmax = [&](int jl) {
+    const char* tb = smem + (jl % 3) * kMlaTile;
+    const int j0 = kbeg + jl * NK;
+    __builtin_amdgcn_s_setprio(1);
+    v4f sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
+#pragma unroll
+    for (int kk = 0; kk < KK; kk += DSA_MLA_QKG) {
+      v8s k0[DSA_MLA_QKG], k1[DSA_MLA_QKG];
+#pragma unroll
+      for (int u = 0; u < DSA_MLA_QKG; ++u) {
+        k0[u] = *(const v8s*)(tb + ((kk + u) * 64 + lane) * 16);
+        k1[u] = *(const v8s*)(tb + ((VF + kk + u) * 64 + lane) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < DSA_MLA_QKG; ++u) {
+        sc0 = mfma_bf16_16x16x32(k0[u], qf[kk + u], sc0);
+        sc1 = mfma_bf16_16x16x32(k1[u], qf[kk + u], sc1);
+      }
+      // all of the group's reads in flight before its first MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DSA_MLA_QKG, 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DSA_MLA_QKG, 0);  // MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // keys past the block's last valid entry (last tile only) drop out
+    if (j0 + NK > n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (j0 + 4 * g + i >= n) sc0[i] = -INFINITY;
+        if (j0 + 16 + 4 * g + i >= n) sc1[i] = -INFINITY;
+      }
+    }
+    // zs > 0, so the max of the scaled scores is the scaled max
+    float mx = fmaxf(fmaxf(fmaxf(sc0[0], sc0[1]), fmaxf(sc0[2], sc0[3])),
+                     fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
+    mx = rows_max(mx) * zs;
+    const bool need = mx > m_run + 8.f;
+    const float mnew = need ? mx : m_run;
+    const float corr = exp2_raw(m_run - mnew);
+    m_run = mnew;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2_raw(fmaf(sc0[i], zs, -mnew));
+      p[4 + i] = exp2_raw(fmaf(sc1[i], zs, -mnew));
+    }
+    v4i pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = (int)pack_bf16x2(p[2 * i], p[2 * i + 1]);
+    l_part = fmaf(l_part, corr, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+    const int par = jl & 1;
+    *(v4i*)(pbuf + ((par * 8 + w) * 64 + lane) * 16) = pk;
+    if (g == 0) s_corr[par][16 * w + c] = corr;
+    const bool any = __any(need);
+    if (lane == 0) s_need[par][w] = any ? 1 : 0;
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // O^T += V^T . P^T of tile jl for all heads over the wave's value
+  // columns, after the rescale of the heads whose max moved in that tile
+  auto pv = [&](int jl) {
+    const int par = jl & 1;
+    const char* tb = smem + (jl % 3) * kMlaTile;
+    bool resc = false;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) resc |= s_need[par][i] != 0;
+    if (resc) {
+#pragma unroll
+      for (int hs = 0; hs < 8; ++hs) {
+        const float cr = s_corr[par][16 * hs + c];
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[d][hs] *= cr;
+      }
+    }
+    v8s av[ND];
+    lds_read_vt4<VF * 1024>(tb + vbase + 2048 * w, av);
+#pragma unroll
+    for (int hs = 0; hs < 8; ++hs) {
+      const v8s pf = *(const v8s*)(pbuf + ((par * 8 + hs) * 64 + lane) * 16);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[d][hs] = mfma_bf16_16x16x32(av[d], pf, o[d][hs]);
+      if (hs % DSA_PV_GROUP == DSA_PV_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // slot 2j: group 0 S^T + softmax of tile j, group 1 PV of tile j-1 (and
+  // the gather of tile j+1); slot 2j+1: group 1 S^T + softmax of tile j,
+  // group 0 PV of tile j-1.  Both groups pass the same 2 ntiles + 2 barriers.
+  if (G == 0) {
+    __syncthreads();
+    for (int jj = 0; jj <= ntiles; ++jj) {
+      if (jj < ntiles) qk_softmax(jj);
+      lds_barrier();
+      if (jj >= 1) pv(jj - 1);
+      lds_barrier();
+    }
+  } else {
+    if (ntiles > 0) issue_tile(0);
+    __syncthreads();  // waits for the first tile
+    for (int jj = 0; jj <= ntiles; ++jj) {
+      if (jj + 1 < ntiles) issue_tile(jj + 1);
+      if (jj >= 1) pv(jj - 1);
+      lds_barrier();
+      if (jj < ntiles) qk_softmax(jj);
+      if (jj + 1 < ntiles) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile jj+1 has landed
+      lds_barrier();
+    }
+  }
+
+  // epilogue: row sums of every head, then lane (c, g) of wave w writes
+  // O^T[dv = 64w + 16d + 4g + i][head 16hs + c]
+  const bool partial = a.splits > 1;
+  {
+    const float l = rows_sum(l_part);
+    if (g == 0) {
+      const int h = 16 * w + c;
+      s_l[h] = l;
+      if (partial) {
+        float* ml = a.part_ml + ((t * a.splits + sp) * H + h) * 2;
+        ml[0] = m_run;
+        ml[1] = l;
+      } else if (a.lse) {
+        a.lse[t * H + h] = n > kbeg ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hs = 0; hs < 8; ++hs) {
+    const int h = 16 * hs + c;
+    if (partial) {
+      float* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + 64 * w;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) *(v4f*)(op + 16 * d + 4 * g) = o[d][hs];
+    } else {
+      const float l = s_l[h];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV + 64 * w;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         v2i pk;
@@ -531,10 +755,11 @@ bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int
   if (f32) return H >= 1 && H <= 64 && Dk >= 4 && Dk <= 128 && Dv >= 4 && Dv <= 128 && Dk % 4 == 0 && Dv % 4 == 0;
   if (H == 16 && Dk == 128 && Dv == 128) return true;
   if (H == 128 && Dk == 576 && Dv == 512) {
-    // two gathered tiles + P^T (+ partial S^T) + the index row must fit in LDS
-    const size_t tile = (size_t)32 * (Dk / 8 + (sep_v ? Dv / 8 : 0)) * 16;
-    const size_t xch = attn_ksplit((int)Dk, 8, sep_v) ? 8 * 2048 : 0;
-    return 2 * tile + 8 * 1024 + xch + (size_t)k * 4 <= kAttnLdsLimit;
+    // shared latent row: three gathered tiles + two P^T sets + the index
+    // row; separate V: two tiles of key and value rows + P^T + the index row
+    if (!sep_v) return kMlaFixedLds + (size_t)k * 4 <= kAttnLdsLimit;
+    const size_t tile = (size_t)32 * (Dk / 8 + Dv / 8) * 16;
+    return 2 * tile + 8 * 1024 + (size_t)k * 4 <= kAttnLdsLimit;
   }
   return false;
 }
@@ -561,7 +786,7 @@ size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t 
 template <int DK, int DV, int NW, bool SEPV>
 static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
   constexpr size_t tile = (size_t)32 * (DK / 8 + (SEPV ? DV / 8 : 0)) * 16;
-  constexpr size_t fixed = 2 * tile + (size_t)NW * 1024 + (attn_ksplit(DK, NW, SEPV) ? (size_t)NW * 2048 : 0);
+  constexpr size_t fixed = 2 * tile + (size_t)NW * 1024;
   constexpr size_t lds_max = fixed + (size_t)DSA_MAX_TOPK * 4 <= kAttnLdsLimit
                                  ? fixed + (size_t)DSA_MAX_TOPK * 4 : kAttnLdsLimit;
   const size_t lds = fixed + (size_t)a.k * 4;
@@ -579,6 +804,29 @@ static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStre
   const int64_t per_blk = 256 / (a.Dv / 4);
   attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
   return hipGetLastError();
+}
+
+static hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
+  const int64_t per_blk = 256 / (a.Dv / 4);
+  attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+static hipError_t launch_mla(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
+  constexpr size_t lds_max = kMlaFixedLds + (size_t)DSA_MAX_TOPK * 4;
+  static_assert(lds_max <= kAttnLdsLimit, "three tiles, P^T and the index row fit in LDS");
+  const size_t lds = kMlaFixedLds + (size_t)a.k * 4;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mla_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds_max);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  attn_mla_kernel<<<(unsigned)(a.T * a.splits), 512, lds, st>>>(a, seq_off);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  return launch_combine(a, st);
 }
 
 hipError_t launch_attn(const AttnArgs& a_in, bool f32, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -601,7 +849,7 @@ hipError_t launch_attn(const AttnArgs& a_in, bool f32, void* ws, size_t ws_bytes
   }
   if (a.H == 128 && a.Dk == 576 && a.Dv == 512) {
     if (a.v) return launch_bf16<576, 512, 8, true>(a, a.seq_offsets, st);
-    return launch_bf16<576, 512, 8, false>(a, a.seq_offsets, st);
+    return launch_mla(a, a.seq_offsets, st);
   }
   return hipErrorInvalidValue;
 }

@@ -181,15 +181,28 @@ def test_sparse_attn(dev, name, spec, k):
 
 
 def test_sparse_attn_separate_v_view(dev):
-    """The latent-row reading (V = first Dv entries of the KV row) equals
-    passing that slice as an explicit V with its own leading dimension."""
+    """The latent-row reading (V = first Dv entries of the KV row, taken by
+    the two-group MLA kernel) and the same columns passed as an explicit V
+    with its own leading dimension (the separate-V kernel) both match the
+    oracle, and agree with each other to one bf16 rounding: the two kernels
+    accumulate in different orders, so their fp32 results differ far below
+    a bf16 unit in the last place (2^-7 relative)."""
     spec = gen.PREFILL_32K.with_(L=600)
     x = gen.make_prefill(spec, seed=6, device=dev)
     idx = gen.make_selection(16, spec.L, 256, seed=7, min_valid=1).to(dev)
     q = x["q"][:16].contiguous()
     a = B.dsa_sparse_attn(q, x["kv"], idx, spec.scale, v=None, Dv=512)
     b = B.dsa_sparse_attn(q, x["kv"], idx, spec.scale, v=x["kv"][:, :512], Dv=512)
-    assert torch.equal(a, b)
+    ga, gb = od.as_f64(to_np(a)), od.as_f64(to_np(b))
+    kv, qn, gi = to_np(x["kv"]), to_np(q), idx.cpu().numpy()
+    for t in range(16):
+        sel = gi[t][gi[t] >= 0]
+        kr = od.as_f64(kv[sel])
+        o, _ = od.attend(od.as_f64(qn[t]), kr, kr[:, :512], spec.scale)
+        P.check_attn(ga[t], o)
+        P.check_attn(gb[t], o)
+    assert np.all(np.abs(ga - gb) <= 2.0 ** -7 * np.maximum(np.abs(ga), np.abs(gb)) + 1e-6)
+    say("differing elements", int(np.sum(ga != gb)), "of", ga.size)
 
 
 # ---------------------------------------------------------- whole forward ---
