@@ -180,6 +180,43 @@ def test_sparse_attn(dev, name, spec, k):
     say("worst", worst)
 
 
+@pytest.mark.parametrize("T", [20, 300], ids=["split", "unsplit"])
+def test_sparse_attn_mla_rescale_and_ragged(dev, T):
+    """The MLA kernel when a later tile raises a head's running max by far
+    more than 2^8 (key rows from position 1000 on scaled by 8, exact in
+    bf16, so the accumulated output must be rescaled mid-row), with valid
+    counts that end inside a tile, at a tile boundary and at 0, both with the
+    key splits of few queries (T = 20) and without them (T = 300); sampled
+    queries and their log-sum-exp against the oracle."""
+    spec = gen.PREFILL_32K.with_(L=2000)
+    x = gen.make_prefill(spec, seed=8, device=dev)
+    kv = x["kv"].clone()
+    kv[1000:] *= 8
+    q = x["q"][:T].contiguous()
+    idx = gen.make_selection(T, spec.L, 2048, seed=9, min_valid=1)
+    counts = {0: 2000, 1: 1, 2: 31, 3: 32, 4: 33, 5: 0, 6: 1023, 7: 1999}
+    for t, m in counts.items():
+        idx[t] = -1
+        if m:
+            idx[t, :m] = torch.arange(2000 - m, 2000, dtype=torch.int32) if t == 2 else torch.arange(m, dtype=torch.int32)
+    lse = torch.empty((T, spec.H), dtype=torch.float32, device=dev)
+    out = B.dsa_sparse_attn(q, kv, idx.to(dev), spec.scale, Dv=spec.Dv, lse_out=lse)
+    g, gl = od.as_f64(to_np(out)), to_np(lse)
+    kvn, qn, gi = to_np(kv), to_np(q), idx.numpy()
+    rows = list(counts) + list(range(8, T, max(1, T // 12)))
+    worst = 0.0
+    for t in rows:
+        sel = gi[t][gi[t] >= 0]
+        if sel.size == 0:
+            assert np.all(g[t] == 0) and np.all(np.isneginf(gl[t])), t
+            continue
+        kr = od.as_f64(kvn[sel])
+        o, l = od.attend(od.as_f64(qn[t]), kr, kr[:, : spec.Dv], spec.scale)
+        worst = max(worst, P.check_attn(g[t], o))
+        assert np.allclose(gl[t], l, rtol=1e-5, atol=1e-4), t
+    say("rows", len(rows), "worst", worst)
+
+
 def test_sparse_attn_separate_v_view(dev):
     """The latent-row reading (V = first Dv entries of the KV row, taken by
     the two-group MLA kernel) and the same columns passed as an explicit V
