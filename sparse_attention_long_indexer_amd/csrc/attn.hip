@@ -607,25 +607,45 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
     }
   }
   __syncthreads();
+  if (partial) {
 #pragma unroll
-  for (int hs = 0; hs < 8; ++hs) {
-    const int h = 16 * hs + c;
-    if (partial) {
+    for (int hs = 0; hs < 8; ++hs) {
+      const int h = 16 * hs + c;
       float* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + 64 * w;
 #pragma unroll
       for (int d = 0; d < ND; ++d) *(v4f*)(op + 16 * d + 4 * g) = o[d][hs];
-    } else {
-      const float l = s_l[h];
+    }
+    return;
+  }
+  // normalised bf16 rows staged in the (now idle) tile buffers, 64 heads at
+  // a time with a padded row stride, then written as whole 1 KB head rows
+  constexpr int kRow = DV * 2 + 16;
+  uint16_t* ob = (uint16_t*)a.out + t * H * (int64_t)DV;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const int hs = 4 * half + hh;
+      const float l = s_l[16 * hs + c];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* op = (uint16_t*)a.out + (t * H + h) * (int64_t)DV + 64 * w;
+      char* sp_row = smem + (16 * hh + c) * kRow + (64 * w + 4 * g) * 2;
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         v2i pk;
         pk[0] = (int)pack_bf16x2(o[d][hs][0] * inv, o[d][hs][1] * inv);
         pk[1] = (int)pack_bf16x2(o[d][hs][2] * inv, o[d][hs][3] * inv);
-        *(v2i*)(op + 16 * d + 4 * g) = pk;
+        *(v2i*)(sp_row + 32 * d) = pk;
       }
     }
+    lds_barrier();
+    // 64 rows x 64 lanes of 16 bytes: wave w writes rows w, w + 8, ...
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int r = 8 * rr + w;
+      const v4i v = *(const v4i*)(smem + r * kRow + 16 * lane);
+      *(v4i*)(ob + (64 * half + r) * (int64_t)DV + 8 * lane) = v;
+    }
+    lds_barrier();
   }
 }
 
