@@ -811,13 +811,9 @@ static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStre
                                  ? fixed + (size_t)DSA_MAX_TOPK * 4 : kAttnLdsLimit;
   const size_t lds = fixed + (size_t)a.k * 4;
   if (lds > lds_max) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<DK, DV, NW, SEPV>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  hipError_t ea = set_lds_limit_once((const void*)attn_bf16_kernel<DK, DV, NW, SEPV>, (int)lds_max, attr_done);
+  if (ea != hipSuccess) return ea;
   attn_bf16_kernel<DK, DV, NW, SEPV><<<(unsigned)(a.T * a.splits), NW * 64, lds, st>>>(a, seq_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
@@ -836,13 +832,9 @@ static hipError_t launch_mla(const AttnArgs& a, const int64_t* seq_off, hipStrea
   constexpr size_t lds_max = kMlaFixedLds + (size_t)DSA_MAX_TOPK * 4;
   static_assert(lds_max <= kAttnLdsLimit, "three tiles, P^T and the index row fit in LDS");
   const size_t lds = kMlaFixedLds + (size_t)a.k * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mla_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds_max);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  hipError_t ea = set_lds_limit_once((const void*)attn_mla_kernel, (int)lds_max, attr_done);
+  if (ea != hipSuccess) return ea;
   attn_mla_kernel<<<(unsigned)(a.T * a.splits), 512, lds, st>>>(a, seq_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;

@@ -354,16 +354,11 @@ hipError_t launch_attn_bwd(const BwdArgs& a, void* ws, hipStream_t st) {
   const size_t lds_ds = 2 * TILE + a.k * 4;
   const size_t lds_dq = 2 * TILE + 2 * kPhTile + a.k * 4;
   const size_t lds_kv = (size_t)(4 * kPhTile > 32 * DK * 2 ? 4 * kPhTile : 32 * DK * 2) + a.k * 4;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_bwd_ds_kernel<DK, DV>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * TILE + 16384));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)attn_bwd_dq_kernel<DK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(2 * TILE + 2 * kPhTile + 16384));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> ds_done{0}, dq_done{0};
+  hipError_t ea = set_lds_limit_once((const void*)attn_bwd_ds_kernel<DK, DV>, (int)(2 * TILE + 16384), ds_done);
+  if (ea != hipSuccess) return ea;
+  ea = set_lds_limit_once((const void*)attn_bwd_dq_kernel<DK>, (int)(2 * TILE + 2 * kPhTile + 16384), dq_done);
+  if (ea != hipSuccess) return ea;
   for (int64_t t0 = 0; t0 < a.T; t0 += C) {
     const unsigned nb = (unsigned)(a.T - t0 < C ? a.T - t0 : C);
     attn_bwd_ds_kernel<DK, DV><<<nb, 512, lds_ds, st>>>(a, t0, pbuf, dsbuf);

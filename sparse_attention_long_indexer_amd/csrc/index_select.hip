@@ -716,13 +716,9 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
   const int64_t bn = S < kSelBitmapN ? S : kSelBitmapN;
   const int64_t words = S > kSelBitmapN && 2 * kOutBuckets > (bn + 31) / 32 ? 2 * kOutBuckets : (bn + 31) / 32;
   const size_t lds = (size_t)2 * kSelMax * 4 + (size_t)words * 4;
-  static bool attr = false;
-  if (!attr) {
-    e = hipFuncSetAttribute((const void*)idx_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(2 * kSelMax * 4 + (kSelBitmapN / 32) * 4));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  e = set_lds_limit_once((const void*)idx_select_kernel, (int)(2 * kSelMax * 4 + (kSelBitmapN / 32) * 4), attr_done);
+  if (e != hipSuccess) return e;
   idx_select_kernel<<<(unsigned)T, kSelThreads, lds, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, fb,
                                                           force_fallback ? 1 : 0, dyn);
   if ((e = hipGetLastError()) != hipSuccess) return e;

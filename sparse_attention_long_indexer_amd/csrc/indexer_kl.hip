@@ -364,13 +364,9 @@ hipError_t launch_indexer_kl(const KlArgs& a, void* ws, hipStream_t st) {
   e = launch_index_scores(qf, nullptr, a.k_idx, nullptr, false, a.L, a.L, nullptr, 0, 0, a.L, gmat, a.L, st);
   if (e != hipSuccess) return e;
   constexpr int TILE = kKNK * (DK / 8 + 1) * 16;
-  static bool attr = false;
-  if (!attr) {
-    e = hipFuncSetAttribute((const void*)kl_target_kernel<DK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            2 * TILE);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  e = set_lds_limit_once((const void*)kl_target_kernel<DK>, 2 * TILE, attr_done);
+  if (e != hipSuccess) return e;
   kl_target_kernel<DK><<<(unsigned)a.L, 512, 2 * TILE, st>>>((const uint16_t*)a.q, (const char*)a.kv, a.ld_kv, a.L,
                                                               a.scale, gmat, a.loss);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -357,13 +357,9 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
   topk_cand_filter_kernel<<<fgrid, 256, 0, st>>>(r, c.tau, c.cand, c.cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   constexpr size_t lds_max = (size_t)kCandCap * 8 + (size_t)(kCandBitmapN / 32) * 4;
-  static bool attr = false;
-  if (!attr) {
-    e = hipFuncSetAttribute((const void*)topk_cand_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds_max);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  e = set_lds_limit_once((const void*)topk_cand_select_kernel, (int)lds_max, attr_done);
+  if (e != hipSuccess) return e;
   const int64_t bm = max_n > kCandBitmapN ? kCandBitmapN : max_n;
   const size_t words = max_n > kCandBitmapN && (size_t)(2 * kOutBuckets) > (size_t)((bm + 31) / 32)
                            ? (size_t)(2 * kOutBuckets)
