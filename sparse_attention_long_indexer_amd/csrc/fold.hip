@@ -8,13 +8,14 @@
 // Work: T x 128 x 128 MACs in fp64 (bit-reproducible codes), ~1/1024 of the
 // indexer's pair work.  One thread owns one output column j and keeps column
 // j of W in registers; a block walks kRows query rows held in LDS as fp64.
+// Short batches split each column's sum over four waves instead.
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 
-// rows per block: 32 for long prefills; small batches (decode) use 2 so the
-// launch still spreads over many CUs
+// kFoldRows query rows per block (32, for long prefills; short batches use
+// fold_split_kernel below)
 template <bool kFp8In, bool kWBf16, int kFoldRows>
 __global__ __launch_bounds__(128) void fold_kernel(const void* __restrict__ q_in,
                                                    const float* __restrict__ q_scale,
@@ -77,6 +78,83 @@ __global__ __launch_bounds__(128) void fold_kernel(const void* __restrict__ q_in
   }
 }
 
+// Short batches (decode): the sum over i is split across four waves per
+// column (32 terms each, in i order), and the four fp64 partials are added
+// in a fixed order.  Two rows per block.
+template <bool kFp8In, bool kWBf16>
+__global__ __launch_bounds__(512) void fold_split_kernel(const void* __restrict__ q_in,
+                                                         const float* __restrict__ q_scale,
+                                                         const void* __restrict__ w_in, int64_t T,
+                                                         void* __restrict__ q_out, float* __restrict__ s_out) {
+  constexpr int R = 2, P = 4, IP = kIdxDim / P;
+  __shared__ double qrow[R][kIdxDim];
+  __shared__ double part[P][R][kIdxDim];
+  __shared__ double wmax[2][R];
+  const int tid = threadIdx.x, j = tid & (kIdxDim - 1), pi = tid / kIdxDim;
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int nr = (int)min<int64_t>(R, T - r0);
+  if (tid < R * kIdxDim) {
+    const int r = tid / kIdxDim;
+    double v = 0.0;
+    if (r < nr) {
+      const int64_t t = r0 + r;
+      if (kFp8In)
+        v = (double)e4m3_to_f32(((const uint8_t*)q_in)[t * kIdxDim + j]) * (double)q_scale[t];
+      else
+        v = (double)((const float*)q_in)[t * kIdxDim + j];
+    }
+    qrow[r][j] = v;
+  }
+  float wcol[IP];
+#pragma unroll
+  for (int ii = 0; ii < IP; ++ii) {
+    const int i = pi * IP + ii;
+    if (kWBf16)
+      wcol[ii] = bf16_to_f32(((const uint16_t*)w_in)[i * kIdxDim + j]);
+    else
+      wcol[ii] = ((const float*)w_in)[i * kIdxDim + j];
+  }
+  __syncthreads();
+  double acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0;
+#pragma unroll
+  for (int ii = 0; ii < IP; ++ii) {
+    const double w = (double)wcol[ii];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fma(qrow[r][pi * IP + ii], w, acc[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) part[pi][r][j] = acc[r];
+  __syncthreads();
+  const bool own = tid < kIdxDim;
+  double sum[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    sum[r] = own ? ((part[0][r][j] + part[1][r][j]) + part[2][r][j]) + part[3][r][j] : 0.0;
+  if (!kFp8In) {
+    if (own)
+      for (int r = 0; r < nr; ++r) ((float*)q_out)[(r0 + r) * kIdxDim + j] = (float)sum[r];
+    return;
+  }
+  // per-row amax over the 128 columns (waves 0 and 1)
+  const int wv = tid >> 6;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const double m = wave_max(fabs(sum[r]));
+    if (wv < 2 && (tid & 63) == 0) wmax[wv][r] = m;
+  }
+  __syncthreads();
+  if (!own) return;
+  for (int r = 0; r < nr; ++r) {
+    const double amax = max(wmax[0][r], wmax[1][r]);
+    const float sc = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+    const uint32_t code = f64_to_e4m3_rne_sat(sum[r] / (double)sc);
+    ((uint8_t*)q_out)[(r0 + r) * kIdxDim + j] = (uint8_t)code;
+    if (j == 0) s_out[r0 + r] = sc;
+  }
+}
+
 template <int R>
 static void launch_fold_rows(const void* q_in, const float* q_scale, bool fp8_in, const void* w, bool w_bf16,
                              int64_t T, void* q_out, float* s_out, hipStream_t st) {
@@ -94,8 +172,15 @@ hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, cons
   if (T <= 0) return hipSuccess;
   if (T >= 8192)
     launch_fold_rows<32>(q_in, q_scale, fp8_in, w, w_bf16, T, q_out, s_out, st);
-  else
-    launch_fold_rows<2>(q_in, q_scale, fp8_in, w, w_bf16, T, q_out, s_out, st);
+  else {
+    dim3 grid((unsigned)((T + 1) / 2));
+    if (fp8_in && w_bf16)
+      fold_split_kernel<true, true><<<grid, 512, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+    else if (fp8_in)
+      fold_split_kernel<true, false><<<grid, 512, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+    else
+      fold_split_kernel<false, false><<<grid, 512, 0, st>>>(q_in, q_scale, w, T, q_out, s_out);
+  }
   return hipGetLastError();
 }
 
