@@ -26,8 +26,10 @@
  *     offsets are int64; key indices are int32.
  *   - FP8 means OCP E4M3 ("e4m3fn": bias 7, max 448, NaN = S.1111.111) with
  *     one fp32 scale per row: value = e4m3(code) * scale[row].
- *   - Thread safety: no mutable global state; calls on different streams may
- *     run concurrently.
+ *   - Devices and threads: a call runs on the caller's current HIP device.
+ *     The only global state is a per-device record of which kernels already
+ *     have their LDS limit raised, updated atomically, so calls from several
+ *     threads, on several streams or devices, may run concurrently.
  */
 #ifndef DSA_H_
 #define DSA_H_
