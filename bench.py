@@ -13,9 +13,15 @@ chunks of --chunk queries over the growing key prefix (a step is all the
 chunks), and a 64-sequence decode over caches of 2^19 .. 2^20 keys.
 
 The dominant kernel's duration is measured live with HIP events on the stream
-the kernel runs on; its roofline uses algorithmic FLOPs (or bytes) only.  The
-CPU baseline times the fp64 oracle on a bounded random sample of query rows of
-the same workload, on this host's cores.
+the kernel runs on; its roofline uses algorithmic FLOPs (or bytes) only, and
+is stated against both the published peak and the peak measured in the same
+run by the probe library (an MFMA issue loop and a streaming HBM read).  GPU
+clocks and power are read before and after the timed region.  The 8K and 32K
+prefills are timed as extra lines; decode is timed warm (one cache set) and
+cold (four cache sets in rotation, 24 GB, far past the 256 MB last-level
+cache).  The CPU baseline times the fp64 oracle on a stratified sample of
+query rows of the same workload with one single-threaded worker process per
+available core, and extrapolates the whole prefill from a per-row cost model.
 """
 from __future__ import annotations
 
@@ -68,6 +74,228 @@ def load_traffic(kernel, sha):
     if not e or e.get("source_sha") != sha:
         return None
     return e.get("bytes_per_launch")
+
+
+def gpu_clocks():
+    """Shader and memory clocks and power of GPU 0 as the system tools report
+    them (amd-smi, else rocm-smi); the raw fields are kept as reported."""
+    import subprocess
+    cmds = [["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"],
+            ["rocm-smi", "-d", "0", "--showclocks", "--showpower", "--json"]]
+    for cmd in cmds:
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except Exception:  # pragma: no cover - tool missing or hung
+            continue
+        if r.returncode != 0 or not r.stdout.strip():
+            continue
+        try:
+            d = json.loads(r.stdout[r.stdout.index(r.stdout.lstrip()[0]):])
+        except Exception:
+            continue
+        flat = {}
+
+        def walk(v, key):
+            if isinstance(v, dict):
+                for k2, v2 in v.items():
+                    walk(v2, f"{key}.{k2}" if key else str(k2))
+            elif isinstance(v, list):
+                for i, v2 in enumerate(v):
+                    walk(v2, f"{key}[{i}]")
+            else:
+                low = key.lower()
+                if any(w in low for w in ("sclk", "mclk", "gfx", "mem", "power", "socket", "clk")):
+                    flat[key] = v
+        walk(d, "")
+        if flat:
+            return {"tool": cmd[0], "fields": dict(list(flat.items())[:40])}
+    return None
+
+
+def probe_peaks(torch, dev):
+    """Achievable peaks measured with the probe library on this GPU: the FP8
+    and bf16 MFMA issue rates (whole chip, 2 blocks of 4 waves per CU) and a
+    streaming read of 4 GiB (16 times the last-level cache), each the best of
+    a few launches timed with HIP events on the stream they run on."""
+    import ctypes
+
+    from sparse_attention_long_indexer_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.dsa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dsa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    lib.dsa_probe_mfma_flops.restype = ctypes.c_double
+    lib.dsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    st = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus
+    sink = torch.empty(blocks * 256 * 4, dtype=torch.float32, device=dev)
+
+    def timed(launch, reps=3):
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            if launch() != 0:
+                raise RuntimeError("probe launch rejected")
+            e1.record(st)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    out = {"method": "probe library: MFMA issue loops (8 independent accumulators per wave, 2 workgroups of "
+                     "4 waves per CU) and a 16-byte-load streaming read of 4 GiB; best of 3 launches"}
+    iters = 4096
+    for kind, key in ((0, "fp8_tflops"), (1, "bf16_16x16x32_tflops"), (2, "bf16_32x32x16_tflops")):
+        lib.dsa_probe_mfma(kind, 16, blocks, ctypes.c_void_p(sink.data_ptr()), sp)   # warm-up
+        ms = timed(lambda: lib.dsa_probe_mfma(kind, iters, blocks, ctypes.c_void_p(sink.data_ptr()), sp))
+        out[key] = round(lib.dsa_probe_mfma_flops(kind, iters, blocks) / (ms * 1e-3) / 1e12, 1)
+    out["bf16_tflops"] = max(out["bf16_16x16x32_tflops"], out["bf16_32x32x16_tflops"])
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    rblocks = 8 * cus
+    rsink = torch.empty(rblocks * 256, dtype=torch.float32, device=dev)
+    lib.dsa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks, ctypes.c_void_p(rsink.data_ptr()), sp)
+    ms = timed(lambda: lib.dsa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks,
+                                          ctypes.c_void_p(rsink.data_ptr()), sp))
+    out["hbm_read_gbps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, rsink, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def stratified_rows(L, k, n, seed=0):
+    """At least n query rows of an L-token prefill: every row below 64, the
+    rows around k and 2k (where the selection stops taking every key), the
+    last 64 rows, and a seeded uniform draw for the rest."""
+    import numpy as np
+    rows = set(range(min(L, 64)))
+    for c in (k, 2 * k):
+        rows |= set(range(max(0, c - 16), min(L, c + 16)))
+    rows |= set(range(max(0, L - 64), L))
+    rng = np.random.default_rng(seed)
+    while len(rows) < min(n, L):
+        rows |= set(rng.integers(0, L, n - len(rows)).tolist())
+    return sorted(rows)
+
+
+_W = {}   # per-worker state of the CPU-baseline pool
+
+
+def _cpu_worker_init(data_dir, topk, scale, Dv):
+    """Pool worker set-up: one BLAS thread, then the oracle of the whole
+    prefill from memory-mapped host copies of the inputs."""
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[v] = "1"
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        _W["limit"] = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+    import oracle.dsa as od
+
+    def ld(name):
+        return np.load(os.path.join(data_dir, name + ".npy"), mmap_mode="r")
+
+    rows = ld("rows")
+    qrows = ld("q_rows")
+    where = {int(t): i for i, t in enumerate(rows)}
+
+    class Q:
+        def __getitem__(self, t):
+            return np.asarray(qrows[where[int(t)]])
+
+    t0 = time.perf_counter()
+    _W["orc"] = od.PrefillOracle(np.asarray(ld("q_idx")), np.asarray(ld("q_scale")), np.asarray(ld("k_idx")),
+                                 np.asarray(ld("k_scale")), np.asarray(ld("w")), Q(), ld("kv"), None, topk, scale, Dv)
+    _W["setup"] = time.perf_counter() - t0
+
+
+def _cpu_worker_rows(rows):
+    out = []
+    for t in rows:
+        t0 = time.perf_counter()
+        _W["orc"].row(int(t))
+        out.append((int(t), time.perf_counter() - t0))
+    return out, _W.get("setup", 0.0)
+
+
+def cpu_baseline_pool(spec, x, min_rows=4096, seed=0, timeout_s=600):
+    """The fp64 oracle timed on this host's cores: N = the available cores
+    (at most 16, the host share of one GPU) single-threaded worker processes
+    (BLAS threads 1) run a stratified sample of >= min_rows query rows.  The
+    whole prefill's time is extrapolated from a least-squares per-row cost
+    model cost(t) = a + b (t + 1) + c m_t (scoring grows with the row's keys,
+    attention with its kept keys m_t = min(k, t + 1)), summed over all L rows
+    and divided over the N workers, plus the worker set-up."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    from concurrent.futures import ProcessPoolExecutor
+
+    import numpy as np
+    import torch
+
+    def np_(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    ncores = len(os.sched_getaffinity(0))
+    nworkers = max(1, min(ncores, 16))
+    rows = stratified_rows(spec.L, spec.topk, min_rows, seed)
+    tmp = tempfile.mkdtemp(prefix="dsa_cpu_baseline_")
+    try:
+        ridx = torch.tensor(rows, dtype=torch.int64, device=x["q"].device)
+        np.save(os.path.join(tmp, "rows.npy"), np.asarray(rows, np.int64))
+        np.save(os.path.join(tmp, "q_rows.npy"), np_(x["q"].index_select(0, ridx)))
+        for name in ("q_idx", "q_scale", "k_idx", "k_scale", "w", "kv"):
+            np.save(os.path.join(tmp, name + ".npy"), np_(x[name]))
+        chunks = [rows[i::nworkers * 4] for i in range(nworkers * 4)]
+        # fresh interpreters (spawn): the workers never touch the GPU; a
+        # worker that dies fails the pool instead of hanging it
+        ctx = mp.get_context("spawn")
+        t0 = time.perf_counter()
+        with ProcessPoolExecutor(nworkers, mp_context=ctx, initializer=_cpu_worker_init,
+                                 initargs=(tmp, spec.topk, spec.scale, spec.Dv)) as pool:
+            res = list(pool.map(_cpu_worker_rows, chunks, timeout=timeout_s))
+        wall = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    per = [r for part, _ in res for r in part]
+    setup = max(s for _, s in res)
+    t = np.array([p[0] for p in per], np.float64)
+    sec = np.array([p[1] for p in per], np.float64)
+    m = np.minimum(spec.topk, t + 1)
+    A = np.stack([np.ones_like(t), t + 1, m], axis=1)
+    coef, *_ = np.linalg.lstsq(A, sec, rcond=None)
+    coef = np.maximum(coef, 0.0)
+    L = spec.L
+    allt = np.arange(L, dtype=np.float64)
+    total_cpu = float(coef[0] * L + coef[1] * np.sum(allt + 1) + coef[2] * np.sum(np.minimum(spec.topk, allt + 1)))
+    est_wall = setup + total_cpu / nworkers
+    return {"value": round(L / est_wall, 3), "unit": "tokens/s", "cores": nworkers, "kind": "oracle",
+            "sample": f"{len(rows)} stratified query rows of the {L}-token prefill (rows 0-63, rows around k and "
+                      f"2k, the last 64, the rest uniform) on {nworkers} single-threaded worker processes; "
+                      f"whole prefill extrapolated from the per-row cost model a + b (t+1) + c min(k, t+1) "
+                      f"fitted to the sample (extrapolated)",
+            "cpu_model": cpu_model(), "cores_available": ncores, "blas_threads_per_worker": 1,
+            "sample_wall_s": round(wall, 2), "worker_setup_s": round(setup, 2),
+            "row_cost_model_s": [float(c) for c in coef], "extrapolated_cpu_s": round(total_cpu, 1),
+            "extrapolated_wall_s": round(est_wall, 1)}
 
 
 def cpu_baseline(spec, x, budget_s=15.0, max_rows=4096, seed=0):
@@ -148,35 +376,68 @@ def profile_attention(spec, x, reps):
     log(f"profiled: 1 copy of {n} bytes, {reps} attention launches")
 
 
-def decode_step_stats(B, gen, torch, dev, ds, lengths=None, reps=20):
+def decode_bytes(n, ds):
+    """Algorithmic HBM bytes of one decode step: every cached index key and
+    its scale (132 B), the kept latent rows (Dk bf16 each), Q and O, and the
+    indices written and read once."""
+    import torch
+    return float(n.sum()) * 132 + float(torch.clamp(n, max=ds.topk).sum()) * ds.Dk * 2 \
+        + ds.B * ds.H * (ds.Dk + ds.Dv) * 2 + 2 * ds.B * ds.topk * 4
+
+
+def decode_step_stats(B, gen, torch, dev, ds, lengths=None, reps=20, cold_copies=4):
     """Time whole decode steps (fold, scores, top-k, attention) with HIP
-    events on the stream the library launches on."""
-    xd = gen.make_decode(ds, seed=0, device=dev, lengths=lengths)
-    dout = torch.empty((ds.B, ds.H, ds.Dv), dtype=torch.bfloat16, device=dev)
-    didx = torch.empty((ds.B, ds.topk), dtype=torch.int32, device=dev)
-    da = B.forward_args(xd, ds.topk, ds.scale, ds.Dv, mode=B.DSA_MODE_DECODE, max_len=int(xd["lengths"].max()))
-    dws = torch.empty(max(B.dsa_forward_workspace_size(da), 256), dtype=torch.uint8, device=dev)
-    for _ in range(3):
+    events on the stream the library launches on.  Warm: one cache set,
+    stepped `reps` times.  Cold: `cold_copies` independent cache sets of the
+    same lengths (different contents and addresses, together far larger than
+    the last-level cache), stepped in rotation, so every step reads its
+    cache from HBM."""
+    if lengths is None:
+        lengths = gen.decode_lengths(ds, 0)
+    sets = []
+    for c in range(max(1, cold_copies)):
+        xd = gen.make_decode(ds, seed=c, device=dev, lengths=lengths)
+        dout = torch.empty((ds.B, ds.H, ds.Dv), dtype=torch.bfloat16, device=dev)
+        didx = torch.empty((ds.B, ds.topk), dtype=torch.int32, device=dev)
+        da = B.forward_args(xd, ds.topk, ds.scale, ds.Dv, mode=B.DSA_MODE_DECODE, max_len=int(lengths.max()))
+        sets.append((xd, dout, didx, da))
+    dws = torch.empty(max(max(B.dsa_forward_workspace_size(s[3]) for s in sets), 256), dtype=torch.uint8,
+                      device=dev)
+    for xd, dout, didx, da in sets:
         B.dsa_forward(da, dout, idx_out=didx, ws=dws)
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(st)
-    for _ in range(reps):
-        B.dsa_forward(da, dout, idx_out=didx, ws=dws)
-    ev1.record(st)
-    torch.cuda.synchronize()
-    dms = ev0.elapsed_time(ev1) / reps
-    n = xd["lengths"]
-    byts = float(n.sum()) * 132 + float(torch.clamp(n, max=ds.topk).sum()) * ds.Dk * 2 \
-        + ds.B * ds.H * (ds.Dk + ds.Dv) * 2 + 2 * ds.B * ds.topk * 4
-    del xd, dout, didx, dws
-    return {"workload": ds.name, "queries_per_s": round(ds.B / (dms * 1e-3), 1),
-            "ms_per_step": round(dms, 4), "keys": int(n.sum()), "algorithmic_bytes": byts,
-            "roofline": {"bound": "hbm", "achieved": round(byts / (dms * 1e-3) / 1e9, 1),
-                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": round(byts / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                         "note": "warm caches; whole decode step"}}
+
+    def run(order):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(st)
+        for i in order:
+            xd, dout, didx, da = sets[i]
+            B.dsa_forward(da, dout, idx_out=didx, ws=dws)
+        ev1.record(st)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / len(order)
+
+    warm_ms = run([0] * reps)
+    cold_ms = run([i % len(sets) for i in range(max(reps, 4 * len(sets)))]) if len(sets) > 1 else None
+    byts = decode_bytes(lengths, ds)
+
+    def roof(ms, note):
+        gbps = byts / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_HBM_GBPS, 4), "note": note}
+
+    ms = cold_ms if cold_ms is not None else warm_ms
+    res = {"workload": ds.name, "queries_per_s": round(ds.B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "keys": int(lengths.sum()), "algorithmic_bytes": byts,
+           "cache_bytes_per_set": float(lengths.sum()) * (132 + ds.Dk * 2),
+           "roofline": roof(ms, f"cold: {len(sets)} cache sets in rotation" if cold_ms is not None
+                            else "warm caches")}
+    res["warm"] = {"ms_per_step": round(warm_ms, 4), "queries_per_s": round(ds.B / (warm_ms * 1e-3), 1),
+                   "roofline": roof(warm_ms, "warm: one cache set stepped repeatedly")}
+    del sets, dws
+    torch.cuda.empty_cache()
+    return res
 
 
 def backward_stats(B, torch, spec, x, idx, out, pairs, reps=3):
@@ -344,7 +605,10 @@ def main():
     ap.add_argument("--workload", default="prefill_L131072_mla")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="row-time budget of the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="row-time budget of the CPU baseline of the 2^20-token workload")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
+    ap.add_argument("--no-extra-configs", action="store_true", help="skip the 8K and 32K prefill lines")
     ap.add_argument("--chunk", type=int, default=131072, help="queries per chunk of the 2^20-token prefill")
     ap.add_argument("--dynamic-theta", type=float, default=None,
                     help="per-query k: keep the keys scoring above this (within [--dynamic-kmin, k])")
@@ -375,93 +639,147 @@ def main():
         bench_long(args, B, gen, torch, dev)
         return
     spec = gen.WORKLOADS[args.workload]
+    peaks = None
+    if not args.no_peaks:
+        log("measured peaks (probe library)")
+        peaks = probe_peaks(torch, dev)
+        log(f"peaks: fp8 {peaks['fp8_tflops']} TF, bf16 {peaks['bf16_tflops']} TF, read {peaks['hbm_read_gbps']} GB/s")
     log("workload", spec.name, "generating inputs")
     x = gen.make_prefill(spec, seed=0, device=dev)
     if args.profile_attn:
         profile_attention(spec, x, args.profile_attn)
         return
+    clocks = {"before": gpu_clocks()}
+    line, idx, out = time_prefill(B, torch, dev, spec, x, args.steps, args.warmup, peaks,
+                                  dyn_theta=args.dynamic_theta, dyn_k_min=args.dynamic_kmin, keep=True)
+    clocks["after"] = gpu_clocks()
+    pairs = line["roofline"]["selected_pairs"]
+    result = {
+        "metric": "DSA prefill tokens/s at L=128K, k=2048",
+        "value": line["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": line["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "dtype_detail": "indexer e4m3 x e4m3 -> fp32 MFMA; attention bf16 -> fp32 MFMA", "data": "synthetic",
+        "config": {"workload": spec.name, "L": spec.L, "topk": spec.topk, "heads": spec.H, "dk": spec.Dk,
+                   "dv": spec.Dv, "batch": 1, "index_dim": 128},
+        "roofline": line["roofline"], "roofline_indexer": line["roofline_indexer"],
+        "measured_peaks": peaks, "clocks": clocks,
+    }
+    if args.dynamic_theta is not None:
+        result["metric"] = "DSA prefill tokens/s at L=128K, dynamic k (theta, k_min .. 2048)"
+        result["config"]["dynamic_k"] = {"theta": args.dynamic_theta, "k_min": args.dynamic_kmin,
+                                         "mean_kept": round(pairs / spec.L, 2)}
+    if args.backward:
+        result["backward"] = backward_stats(B, torch, spec, x, idx, out, pairs, reps=max(2, args.steps))
+    del out, idx
+    torch.cuda.empty_cache()
+
+    if not args.no_extra_configs and args.dynamic_theta is None and spec is gen.PREFILL_128K:
+        result["other_prefills"] = {}
+        for extra in (gen.PREFILL_8K, gen.PREFILL_32K):
+            log("workload", extra.name, "generating inputs")
+            xe = gen.make_prefill(extra, seed=0, device=dev)
+            result["other_prefills"][extra.name] = time_prefill(B, torch, dev, extra, xe, max(args.steps, 5),
+                                                                args.warmup, peaks)[0]
+            del xe
+            torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        log("decode: generating inputs (warm: one cache set; cold: four in rotation)")
+        result["decode"] = decode_step_stats(B, gen, torch, dev, gen.DECODE_64, cold_copies=4)
+        if peaks:
+            r = result["decode"]["roofline"]
+            r["frac_measured_peak"] = round(r["achieved"] / peaks["hbm_read_gbps"], 4)
+        log(f"decode cold {result['decode']['ms_per_step']:.3f} ms/step, "
+            f"warm {result['decode']['warm']['ms_per_step']:.3f} ms/step")
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, process pool)")
+        result["cpu_baseline"] = cpu_baseline_pool(spec, x)
+        log(f"cpu baseline {result['cpu_baseline']['value']} tokens/s on {result['cpu_baseline']['cores']} workers")
+    print(json.dumps(result), flush=True)
+
+
+def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, dyn_k_min=0, keep=False):
+    """Whole dsa_forward steps on one prefill workload (wall clock around
+    `steps` steps between synchronisations), then the dominant kernel alone
+    (sparse attention over the step's selection) and the fold alone, each
+    timed with HIP events on the stream the library launches on.  The
+    indexer stage is the step minus attention; its FLOPs are the causal
+    pairs' 2 x 128 each."""
     L, k = spec.L, spec.topk
     out = torch.empty((L, spec.H, spec.Dv), dtype=x["q"].dtype, device=dev)
     idx = torch.empty((L, k), dtype=torch.int32, device=dev)
-    fa = B.forward_args(x, k, spec.scale, spec.Dv, dyn_theta=args.dynamic_theta, dyn_k_min=args.dynamic_kmin)
+    fa = B.forward_args(x, k, spec.scale, spec.Dv, dyn_theta=dyn_theta, dyn_k_min=dyn_k_min)
     ws = torch.empty(max(B.dsa_forward_workspace_size(fa), 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step():
         B.dsa_forward(fa, out, idx_out=idx, ws=ws)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"{spec.name}: warmup {warmup}")
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
+    log(f"{spec.name}: timing {steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
-    tok_s = L / dt
-    log(f"prefill {dt * 1e3:.2f} ms/step, {tok_s:.4g} tokens/s")
+    dt = (time.perf_counter() - t0) / steps
+    log(f"{spec.name}: prefill {dt * 1e3:.2f} ms/step, {L / dt:.4g} tokens/s")
+    del ws
 
-    # dominant kernel (sparse attention) timed alone with HIP events on the
-    # stream it is launched on (torch's current stream, passed to the library)
     st = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = max(2, args.steps)
-    B.dsa_sparse_attn(x["q"], x["kv"], idx, spec.scale, v=x["v"], Dv=spec.Dv, out=out)
-    ev0.record(st)
-    for _ in range(reps):
-        B.dsa_sparse_attn(x["q"], x["kv"], idx, spec.scale, v=x["v"], Dv=spec.Dv, out=out)
-    ev1.record(st)
-    torch.cuda.synchronize()
-    attn_ms = ev0.elapsed_time(ev1) / reps
+
+    def events(fn, reps):
+        fn()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(st)
+        for _ in range(reps):
+            fn()
+        ev1.record(st)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    reps = max(2, steps)
+    attn_ms = events(lambda: B.dsa_sparse_attn(x["q"], x["kv"], idx, spec.scale, v=x["v"], Dv=spec.Dv, out=out),
+                     reps)
+    qf = torch.empty_like(x["q_idx"])
+    qs = torch.empty(L, dtype=torch.float32, device=dev)
+    fold_ms = events(lambda: B.dsa_fold_index_query(x["q_idx"], x["q_scale"], x["w"], qf, qs), reps)
+    del qf, qs
     flops, pairs = attn_flops(L, k, spec.H, spec.Dk, spec.Dv)
-    if args.dynamic_theta is not None:  # the pairs the per-query budgets kept
+    if dyn_theta is not None:  # the pairs the per-query budgets kept
         pairs = int((idx >= 0).sum())
         flops = 2.0 * spec.H * (spec.Dk + spec.Dv) * pairs
     achieved = flops / (attn_ms * 1e-3) / 1e12
+    kern = "attn_mla_kernel" if (spec.H, spec.Dk, spec.Dv) == (128, 576, 512) and x["v"] is None \
+        else "attn_bf16_kernel"
     sha = kernel_source_sha(["attn.hip", "common.h", "kernels.h"])
-    traffic = load_traffic("attn_mla_kernel", sha)
-    roof = {"bound": "mfma", "kernel": "attn_mla_kernel", "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic, "ms_per_launch": round(attn_ms, 3),
-            "algorithmic_flops_per_launch": flops, "selected_pairs": pairs}
+    traffic = load_traffic(kern, sha) if spec is not None and L == 131072 else None
+    roof = {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "ms_per_launch": round(attn_ms, 3), "algorithmic_flops_per_launch": flops, "selected_pairs": pairs}
     idx_ms = dt * 1e3 - attn_ms
     ifl = indexer_flops(L)
-    roof_idx = {"bound": "mfma", "stage": "fold + indexer scores + top-k (forward minus attention)",
-                "ms": round(idx_ms, 3), "achieved": round(ifl / (idx_ms * 1e-3) / 1e12, 2),
-                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ifl / (idx_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
-    log(f"attention {attn_ms:.2f} ms/launch = {achieved:.1f} TFLOP/s; indexer+select {idx_ms:.2f} ms")
-
-    result = {
-        "metric": "DSA prefill tokens/s at L=128K, k=2048",
-        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "dtype_detail": "indexer e4m3 x e4m3 -> fp32 MFMA; attention bf16 -> fp32 MFMA",
-        "data": "synthetic",
-        "config": {"workload": spec.name, "L": L, "topk": k, "heads": spec.H, "dk": spec.Dk, "dv": spec.Dv,
-                   "batch": 1, "index_dim": 128},
-        "roofline": roof, "roofline_indexer": roof_idx,
-    }
-    if args.dynamic_theta is not None:
-        result["metric"] = "DSA prefill tokens/s at L=128K, dynamic k (theta, k_min .. 2048)"
-        result["config"]["dynamic_k"] = {"theta": args.dynamic_theta, "k_min": args.dynamic_kmin,
-                                         "mean_kept": round(pairs / L, 2)}
-    if args.backward:
-        result["backward"] = backward_stats(B, torch, spec, x, idx, out, pairs, reps=max(2, args.steps))
-    del out, idx, ws
-
-    if not args.no_decode:
-        log("decode: generating inputs")
-        result["decode"] = decode_step_stats(B, gen, torch, dev, gen.DECODE_64)
-        log(f"decode {result['decode']['ms_per_step']:.3f} ms/step")
-
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(spec, x, budget_s=args.cpu_seconds)
-    print(json.dumps(result), flush=True)
-
+    idx_tf = ifl / (idx_ms * 1e-3) / 1e12
+    roof_idx = {"bound": "mfma", "stage": "fold + indexer scores + top-k (step minus attention)",
+                "ms": round(idx_ms, 3), "fold_ms": round(fold_ms, 3), "scores_and_select_ms": round(idx_ms - fold_ms, 3),
+                "achieved": round(idx_tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(idx_tf / PEAK_FP8_TFLOPS, 4), "algorithmic_flops": ifl,
+                "note": "per-kernel times of the stage are in the committed rocprofv3 kernel trace"}
+    if peaks:
+        roof["frac_measured_peak"] = round(achieved / peaks["bf16_tflops"], 4)
+        roof_idx["frac_measured_peak"] = round(idx_tf / peaks["fp8_tflops"], 4)
+    log(f"{spec.name}: attention {attn_ms:.2f} ms/launch = {achieved:.1f} TFLOP/s; indexer stage {idx_ms:.2f} ms "
+        f"(fold {fold_ms:.3f} ms)")
+    line = {"tokens_per_s": round(L / dt, 1), "ms_per_step": round(dt * 1e3, 3), "L": L, "topk": k,
+            "heads": spec.H, "dk": spec.Dk, "dv": spec.Dv, "roofline": roof, "roofline_indexer": roof_idx}
+    if keep:
+        return line, idx, out
+    del idx, out
+    return line, None, None
 
 if __name__ == "__main__":
     main()

@@ -157,32 +157,40 @@ def dsa_index_scores(qf, qf_scale, k_idx, k_scale, q_pos=None, row_begin=0, row_
     return out
 
 
-def dsa_topk(scores, k, S=None, q_pos=None, idx_out=None, count_out=None, stream=None):
+def _workspace(ws, nbytes, device, minimum=1):
+    """The caller's workspace tensor, or a fresh one of the queried size."""
+    if ws is None:
+        ws = torch.empty(max(nbytes, minimum), dtype=torch.uint8, device=device)
+    return ws
+
+
+def dsa_topk(scores, k, S=None, q_pos=None, idx_out=None, count_out=None, stream=None, ws=None):
     T, ld = scores.shape
     S = ld if S is None else S
     if idx_out is None:
         idx_out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     wsb = lib().dsa_topk_workspace_size(T, S, k)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=scores.device)
+    ws = _workspace(ws, wsb, scores.device)
     _check("dsa_topk", lib().dsa_topk(_p(scores), ld, T, S, _p(q_pos), k, _p(idx_out), _p(count_out), _p(ws),
                                       wsb, _stream(stream)))
     return idx_out
 
 
-def dsa_topk_dynamic(scores, k_max, k_min, theta, S=None, q_pos=None, idx_out=None, count_out=None, stream=None):
+def dsa_topk_dynamic(scores, k_max, k_min, theta, S=None, q_pos=None, idx_out=None, count_out=None, stream=None,
+                     ws=None):
     T, ld = scores.shape
     S = ld if S is None else S
     if idx_out is None:
         idx_out = torch.empty((T, k_max), dtype=torch.int32, device=scores.device)
     wsb = lib().dsa_topk_workspace_size(T, S, k_max)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=scores.device)
+    ws = _workspace(ws, wsb, scores.device)
     _check("dsa_topk_dynamic", lib().dsa_topk_dynamic(_p(scores), ld, T, S, _p(q_pos), k_max, k_min,
                                                       ctypes.c_float(theta), _p(idx_out), _p(count_out), _p(ws),
                                                       wsb, _stream(stream)))
     return idx_out
 
 
-def dsa_sparse_attn(q, kv, idx, scale, v=None, Dv=None, out=None, lse_out=None, stream=None):
+def dsa_sparse_attn(q, kv, idx, scale, v=None, Dv=None, out=None, lse_out=None, stream=None, ws=None):
     T, H, Dk = q.shape
     S = kv.shape[0]
     Dv = (v.shape[1] if v is not None else Dk) if Dv is None else Dv
@@ -191,14 +199,14 @@ def dsa_sparse_attn(q, kv, idx, scale, v=None, Dv=None, out=None, lse_out=None, 
     if out is None:
         out = torch.empty((T, H, Dv), dtype=q.dtype, device=q.device)
     wsb = lib().dsa_sparse_attn_workspace_size(T, H, Dv, k, dt)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    ws = _workspace(ws, wsb, q.device)
     _check("dsa_sparse_attn", lib().dsa_sparse_attn(
         _p(q), T, H, Dk, dt, _p(kv), kv.stride(0), _p(v), v.stride(0) if v is not None else 0, Dv, S, _p(idx), k,
         ctypes.c_float(scale), _p(out), _p(lse_out), _p(ws), wsb, _stream(stream)))
     return out
 
 
-def dsa_sparse_attn_bwd(q, kv, idx, scale, out, lse, d_out, Dv, dq=None, dkv=None, stream=None):
+def dsa_sparse_attn_bwd(q, kv, idx, scale, out, lse, d_out, Dv, dq=None, dkv=None, stream=None, ws=None):
     """dq (bf16, written) and dkv (fp32, accumulated; zeroed here when not
     given) of the shared-latent sparse attention."""
     T, H, Dk = q.shape
@@ -209,14 +217,14 @@ def dsa_sparse_attn_bwd(q, kv, idx, scale, out, lse, d_out, Dv, dq=None, dkv=Non
     if dkv is None:
         dkv = torch.zeros((S, Dk), dtype=torch.float32, device=q.device)
     wsb = lib().dsa_sparse_attn_bwd_workspace_size(T, H, k)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=q.device)
+    ws = _workspace(ws, wsb, q.device, 256)
     _check("dsa_sparse_attn_bwd", lib().dsa_sparse_attn_bwd(
         _p(q), T, H, Dk, _dtype_code(q), _p(kv), kv.stride(0), Dv, S, _p(idx), k, ctypes.c_float(scale), _p(out),
         _p(lse), _p(d_out), _p(dq), _p(dkv), dkv.stride(0), _p(ws), ws.numel(), _stream(stream)))
     return dq, dkv
 
 
-def dsa_indexer_kl(q_idx, k_idx, w, q, kv, scale, stream=None):
+def dsa_indexer_kl(q_idx, k_idx, w, q, kv, scale, stream=None, ws=None):
     """Per-query KL losses and the gradients (dq_idx, dk_idx, dw) of the
     indexer alignment; all fp32 except the bf16 attention operands."""
     L, H, Dk = q.shape
@@ -226,7 +234,7 @@ def dsa_indexer_kl(q_idx, k_idx, w, q, kv, scale, stream=None):
     dk_idx = torch.empty((L, 128), dtype=torch.float32, device=dev)
     dw = torch.empty((128, 128), dtype=torch.float32, device=dev)
     wsb = lib().dsa_indexer_kl_workspace_size(L)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    ws = _workspace(ws, wsb, dev, 256)
     _check("dsa_indexer_kl", lib().dsa_indexer_kl(
         _p(q_idx), _p(k_idx), _p(w), _p(q), H, Dk, _dtype_code(q), _p(kv), kv.stride(0), L, ctypes.c_float(scale),
         _p(loss), _p(dq_idx), _p(dk_idx), _p(dw), _p(ws), ws.numel(), _stream(stream)))

@@ -404,6 +404,16 @@ dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out,
     float* sc = (float*)(base + p.sc_off);
     const bool fp8 = a->idx_dtype == DSA_FP8_E4M3;
     const int64_t R = a->T;
+    // the plan's regions follow one another inside the workspace
+    DSA_DEBUG_CHECK(p.qf_off + (size_t)R * 128 * (fp8 ? 1 : 4) <= p.qs_off);
+    DSA_DEBUG_CHECK(p.qs_off + (size_t)R * 4 <= p.idx_off);
+    DSA_DEBUG_CHECK(idx_out || p.idx_off + (size_t)R * (size_t)a->topk * 4 <= p.sc_off);
+    DSA_DEBUG_CHECK(!p.fused || p.sc_off + index_select_workspace_bytes(R, prefill_keys(a)) <= p.total);
+    DSA_DEBUG_CHECK(p.fused || a->mode != DSA_MODE_PREFILL ||
+                    (p.chunk_rows >= 1 && p.sc_off + (size_t)p.chunk_rows * (size_t)prefill_keys(a) * 4 <= p.total));
+    DSA_DEBUG_CHECK(a->mode != DSA_MODE_DECODE ||
+                    (p.sc_off + (size_t)a->total_keys * 4 <= p.topk_off && p.topk_off + p.topk_bytes <= p.total));
+    DSA_DEBUG_CHECK(p.total + attn_ws <= ws_bytes);
     const DynK dyn = (a->flags & DSA_FLAG_DYNAMIC_K) ? DynK{a->dyn_theta, a->dyn_k_min} : kFixedK;
 
     hipError_t e = launch_fold(a->q_idx, a->q_scale, fp8, a->w_index, a->w_dtype == DSA_BF16, R, qf,

@@ -849,6 +849,7 @@ hipError_t launch_attn(const AttnArgs& a_in, bool f32, void* ws, size_t ws_bytes
     if (!ws || ws_bytes < attn_workspace_bytes(f32, a.T, a.H, a.Dv, a.k)) return hipErrorInvalidValue;
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + ((size_t)a.T * a.splits * a.H * a.Dv * 4 + 255) / 256 * 256);
+    DSA_DEBUG_CHECK((char*)(a.part_ml + (size_t)a.T * a.splits * a.H * 2) <= (char*)ws + ws_bytes);
   }
   if (f32) {
     a.splits = 1;

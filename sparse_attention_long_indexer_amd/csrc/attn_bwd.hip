@@ -350,6 +350,7 @@ hipError_t launch_attn_bwd(const BwdArgs& a, void* ws, hipStream_t st) {
   const int64_t C = attn_bwd_chunk(a.T, a.k);
   uint16_t* pbuf = (uint16_t*)ws;
   uint16_t* dsbuf = (uint16_t*)((char*)ws + (size_t)(C * a.k * kBH * 2 + 255) / 256 * 256);
+  DSA_DEBUG_CHECK((char*)(dsbuf + (size_t)C * a.k * kBH) <= (char*)ws + attn_bwd_workspace_bytes(a.T, a.k));
   constexpr int TILE = kBNK * (DK / 8 + 1) * 16;
   const size_t lds_ds = 2 * TILE + a.k * 4;
   const size_t lds_dq = 2 * TILE + 2 * kPhTile + a.k * 4;

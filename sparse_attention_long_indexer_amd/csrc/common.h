@@ -34,6 +34,7 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kIdxDim = 128;
 constexpr int kWave = 64;
+constexpr int64_t kMaxGridY = 65535;  // blocks along a grid's y (and z) extent
 
 // ---- number formats ------------------------------------------------------
 

@@ -96,19 +96,26 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
                                int64_t row_begin, int64_t row_end, float* out, int64_t ld,
                                hipStream_t st) {
   (void)T;
-  const int64_t rows = row_end - row_begin;
-  if (rows <= 0 || S <= 0) return hipSuccess;
-  if (fp8) {
-    dim3 grid((unsigned)((S + kKeysPerBlock - 1) / kKeysPerBlock),
-              (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    index_scores_fp8_kernel<<<grid, 256, 0, st>>>((const uint8_t*)qf, qs, (const uint8_t*)k, ks, S,
-                                                   q_pos, pos_base, row_begin, row_end, out, ld);
-  } else {
-    dim3 grid((unsigned)((S + 15) / 16), (unsigned)((rows + 15) / 16));
-    index_scores_f32_kernel<<<grid, 256, 0, st>>>((const float*)qf, (const float*)k, S, q_pos,
-                                                   pos_base, row_begin, row_end, out, ld);
+  if (row_end <= row_begin || S <= 0) return hipSuccess;
+  // row blocks run along the grid's y extent (at most 65535 per launch)
+  const int64_t per_block = fp8 ? kRowsPerBlock : 16;
+  const int64_t per_launch = (int64_t)kMaxGridY * per_block;
+  for (int64_t r0 = row_begin; r0 < row_end; r0 += per_launch) {
+    const int64_t r1 = row_end - r0 < per_launch ? row_end : r0 + per_launch;
+    float* o = out + (r0 - row_begin) * ld;
+    if (fp8) {
+      dim3 grid((unsigned)((S + kKeysPerBlock - 1) / kKeysPerBlock), (unsigned)((r1 - r0 + per_block - 1) / per_block));
+      index_scores_fp8_kernel<<<grid, 256, 0, st>>>((const uint8_t*)qf, qs, (const uint8_t*)k, ks, S, q_pos,
+                                                     pos_base, r0, r1, o, ld);
+    } else {
+      dim3 grid((unsigned)((S + 15) / 16), (unsigned)((r1 - r0 + per_block - 1) / per_block));
+      index_scores_f32_kernel<<<grid, 256, 0, st>>>((const float*)qf, (const float*)k, S, q_pos, pos_base, r0, r1, o,
+                                                     ld);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 // ---- decode: one query per sequence against its own cache ----------------
@@ -123,11 +130,11 @@ constexpr int kDecKeysPerBlock = 4 * kDecWaveKeys;
 
 __global__ __launch_bounds__(256) void index_scores_decode_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k,
-    const float* __restrict__ ks, const int64_t* __restrict__ off, float* __restrict__ out) {
+    const float* __restrict__ ks, const int64_t* __restrict__ off, int64_t b0, float* __restrict__ out) {
   constexpr int J = kDecWaveKeys / 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t b = blockIdx.y;
+  const int64_t b = b0 + blockIdx.y;
   const int64_t lo = off[b], n = off[b + 1] - lo;
   const int64_t sw = (int64_t)blockIdx.x * kDecKeysPerBlock + w * kDecWaveKeys;
   if (sw >= n) return;
@@ -158,9 +165,15 @@ hipError_t launch_index_scores_decode(const uint8_t* qf, const float* qs, const 
                                       const float* ks, const int64_t* offsets, int64_t B,
                                       int64_t max_len, float* out, hipStream_t st) {
   if (B <= 0 || max_len <= 0) return hipSuccess;
-  dim3 grid((unsigned)((max_len + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)B);
-  index_scores_decode_kernel<<<grid, 256, 0, st>>>(qf, qs, k, ks, offsets, out);
-  return hipGetLastError();
+  // sequences run along the grid's y extent (at most 65535 per launch)
+  for (int64_t b0 = 0; b0 < B; b0 += kMaxGridY) {
+    const int64_t nb = B - b0 < kMaxGridY ? B - b0 : kMaxGridY;
+    dim3 grid((unsigned)((max_len + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)nb);
+    index_scores_decode_kernel<<<grid, 256, 0, st>>>(qf, qs, k, ks, offsets, b0, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace dsa

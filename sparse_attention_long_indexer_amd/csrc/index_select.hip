@@ -701,6 +701,8 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
   int32_t* cnt = (int32_t*)take((size_t)T * kSets * kSeg * 4);
   int32_t* fb = (int32_t*)take((size_t)(T + 1) * 4);
   float* scratch = (float*)take((size_t)kFbBlocks * S * 4);
+  DSA_DEBUG_CHECK((size_t)(p - (char*)ws) <= index_select_workspace_bytes(T, S));
+  DSA_DEBUG_CHECK(filter_items(T, S) >= 1 && filter_items(T, S) <= INT32_MAX);
   zero_i32_kernel<<<1, 64, 0, st>>>(fb, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -359,6 +359,7 @@ hipError_t launch_indexer_kl(const KlArgs& a, void* ws, hipStream_t st) {
   float* gmat = (float*)p;
   p += up((size_t)a.L * a.L * 4);
   float* dw_part = (float*)p;
+  DSA_DEBUG_CHECK((char*)(dw_part + (size_t)kDwParts * 128 * 128) <= (char*)ws + indexer_kl_workspace_bytes(a.L));
   hipError_t e = launch_fold(a.q_idx, nullptr, false, a.w, false, a.L, qf, nullptr, st);
   if (e != hipSuccess) return e;
   e = launch_index_scores(qf, nullptr, a.k_idx, nullptr, false, a.L, a.L, nullptr, 0, 0, a.L, gmat, a.L, st);

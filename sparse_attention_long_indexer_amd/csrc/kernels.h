@@ -6,6 +6,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Debug builds (-DDSA_DEBUG) check the launch plans on the host: each
+// workspace carve-up ends inside the size its *_workspace_bytes() query
+// reports, and the plan's derived sizes are in range.  A failed check prints
+// the condition and aborts before anything is launched.
+#ifdef DSA_DEBUG
+#include <cstdio>
+#include <cstdlib>
+#define DSA_DEBUG_CHECK(cond)                                                                   \
+  do {                                                                                          \
+    if (!(cond)) {                                                                              \
+      std::fprintf(stderr, "DSA_DEBUG check failed: %s (%s:%d)\n", #cond, __FILE__, __LINE__); \
+      std::abort();                                                                             \
+    }                                                                                           \
+  } while (0)
+#else
+#define DSA_DEBUG_CHECK(cond) ((void)0)
+#endif
+
 namespace dsa {
 
 // fold.hip

@@ -322,17 +322,18 @@ struct CandWs {
   uint2* cand;
 };
 
+// byte offsets of the candidate path's buffers; returns the bytes used
 static size_t cand_layout(int64_t rows, char* base, CandWs* out) {
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += (bytes + 255) / 256 * 256;
-    return base + at;
+    return at;
   };
-  char* tau = take((size_t)rows * 4);
-  char* cnt = take((size_t)rows * 4);
-  char* cand = take((size_t)rows * kCandCap * 8);
-  if (out) *out = CandWs{(uint32_t*)tau, (int32_t*)cnt, (uint2*)cand};
+  const size_t tau = take((size_t)rows * 4);
+  const size_t cnt = take((size_t)rows * 4);
+  const size_t cand = take((size_t)rows * kCandCap * 8);
+  if (out) *out = CandWs{(uint32_t*)(base + tau), (int32_t*)(base + cnt), (uint2*)(base + cand)};
   return off;
 }
 
@@ -349,7 +350,9 @@ hipError_t launch_topk(const TopkRows& r, int64_t rows, int64_t max_n, int64_t k
     return hipGetLastError();
   }
   CandWs c;
-  cand_layout(rows, (char*)ws, &c);
+  const size_t used = cand_layout(rows, (char*)ws, &c);
+  DSA_DEBUG_CHECK(used <= topk_workspace_bytes(rows, max_n, k));
+  (void)used;
   topk_cand_estimate_kernel<<<(unsigned)rows, kCandThreads, 0, st>>>(r, k, c.tau, c.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -76,3 +76,19 @@ def check_attn(g, o, f32=False):
     rel = np.max(err, axis=-1) / np.maximum(rms, 1e-30)
     assert np.all(rel <= 2e-2), float(np.max(rel))
     return float(np.max(rel))
+
+
+def check_forward_row(g_idx, o_scores, o_sel, k, attend, g_out, f32=False):
+    """One query of a whole forward: the kept indices under the window rule,
+    then its attention output.  The output is held to the oracle's fp64
+    attention over the GPU's own kept set: that is the oracle's set when the
+    two agree, and otherwise a set that differs only inside the boundary
+    window (so every sampled row's output is checked).  `attend(sel)` returns
+    the oracle's (o, lse) over the key indices `sel`.
+    Returns (index differences, worst attention error)."""
+    d = check_topk_row(g_idx, o_scores, o_sel, k)
+    g = np.asarray(g_idx)
+    m = min(k, o_scores.shape[0])
+    sel = np.asarray(o_sel) if d == 0 else g[:m]
+    o, _ = attend(sel)
+    return d, check_attn(g_out, o, f32=f32)

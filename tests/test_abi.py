@@ -32,6 +32,29 @@ def test_exports_every_declared_symbol(lib):
     assert sorted(B.EXPORTED) == names
 
 
+def test_probe_library_exports(lib):
+    """The achievable-peak probe library exports what include/dsa_probe.h
+    declares, and rejects invalid arguments without launching."""
+    from sparse_attention_long_indexer_amd import build as b
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "dsa_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(dsa_probe_[a-z_]+)\s*\(", src)))
+    assert names == ["dsa_probe_mfma", "dsa_probe_mfma_flops", "dsa_probe_read"]
+    probe = ctypes.CDLL(b.PROBE_LIB)
+    for n in names:
+        assert hasattr(probe, n), n
+    probe.dsa_probe_mfma_flops.restype = ctypes.c_double
+    probe.dsa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    assert probe.dsa_probe_mfma_flops(0, 10, 2) == 65536.0 * 8 * 4 * 10 * 2
+    assert probe.dsa_probe_mfma_flops(3, 10, 2) == 0.0
+    probe.dsa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert probe.dsa_probe_mfma(7, 10, 2, _vp(), None) == -1
+    assert probe.dsa_probe_mfma(0, 10, 2, None, None) == -1
+    probe.dsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    assert probe.dsa_probe_read(_vp(), 4096 * 3 + 8, 1, _vp(), None) == -1     # not a multiple of 16
+    assert probe.dsa_probe_read(_vp(), 4096 * 3, 2, _vp(), None) == -1        # not whole rounds of the grid
+
+
 def test_abi_version_and_status_strings(lib):
     assert lib.dsa_abi_version() == 5
     for s in range(7):

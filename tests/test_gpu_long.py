@@ -128,12 +128,9 @@ def test_prefill_chunk_1m(dev):
     diffs = 0
     for t in (0, 1, 499, T - 2, T - 1):
         sc = orc.scores_row(t)
-        sel = od.topk_row(sc, spec.topk)
-        d = P.check_topk_row(gi[t], sc, sel, spec.topk)
+        d, _ = P.check_forward_row(gi[t], sc, od.topk_row(sc, spec.topk), spec.topk,
+                                   lambda sel: orc.attend_row(t, sel), od.as_f64(to_np(o_f[t])))
         diffs += d
-        if d == 0:
-            o, _ = orc.attend_row(t, sel)
-            P.check_attn(od.as_f64(to_np(o_f[t])), o)
     say("window diffs", diffs)
     assert diffs <= 1
 
@@ -152,15 +149,19 @@ def test_decode_1m(dev):
     dec = od.DecodeOracle(n["q_idx"], n["q_scale"], n["k_idx"], n["k_scale"], n["w"], RowsOf(x["q"]),
                           RowsOf(x["kv"]), None, n["offsets"], spec.topk, spec.scale, spec.Dv)
     gi = idx.cpu().numpy()
+    off = n["offsets"]
     diffs = 0
     for b in range(spec.B):
         sc = dec.scores_seq(b)
-        sel = od.topk_row(sc, spec.topk)
-        d = P.check_topk_row(gi[b], sc, sel, spec.topk)
+        lo = int(off[b])
+
+        def attend(sel, b=b, lo=lo):
+            rows = od.as_f64(to_np(x["kv"][lo + torch.as_tensor(np.asarray(sel, np.int64))]))
+            return od.attend(od.as_f64(to_np(x["q"][b])), rows, rows[:, : spec.Dv], spec.scale)
+
+        d, _ = P.check_forward_row(gi[b], sc, od.topk_row(sc, spec.topk), spec.topk, attend,
+                                   od.as_f64(to_np(out[b])))
         diffs += d
-        if d == 0:
-            _, o, _ = dec.seq(b)
-            P.check_attn(od.as_f64(to_np(out[b])), o)
     say("decode window diffs", diffs)
     # differing keys lie inside the boundary window (checked above); longer
     # rows hold more keys within the window's fp32-vs-fp64 margin
