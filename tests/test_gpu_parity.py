@@ -270,26 +270,27 @@ def test_forward_prefill(dev, spec):
     orc = oracle_prefill(spec, x)
     rows = list(range(spec.L)) if spec.L <= 1000 else sample_rows(spec.L, spec.topk, n=24)
     gi = idx.cpu().numpy()
+    qf, qs = B.dsa_fold_index_query(x["q_idx"], x["q_scale"], x["w"])
     diffs = 0
     worst = 0.0
+    nrm = 0.0
     for t in rows:
         sc = orc.scores_row(t)
+        # zero tolerance: the kept set is the exact top-k of the GPU's own
+        # fp32 scores (materialised for this row), under the same order
+        gs = to_np(B.dsa_index_scores(qf, qs, x["k_idx"], x["k_scale"], row_begin=t, row_end=t + 1))[0]
+        assert np.array_equal(gi[t], od.pad_idx(od.topk_row(gs[: t + 1].astype(np.float64), spec.topk), spec.topk)), t
+        nrm = max(nrm, P.check_scores_row(gs, sc, t))
         g = to_np(out[t])
         g = od.as_f64(g) if g.dtype == np.uint16 else g.astype(np.float64)
         d, e = P.check_forward_row(gi[t], sc, od.topk_row(sc, spec.topk), spec.topk,
                                    lambda sel: orc.attend_row(t, sel), g, f32=spec.attn_f32)
         diffs += d
         worst = max(worst, e)
-    say(f"rows={len(rows)} window-diffs={diffs} worst-attn={worst:.3g}")
-    assert diffs <= max(2, len(rows) // 10)
-    if spec.L >= 131072:
-        del out
-        qf, qs = B.dsa_fold_index_query(x["q_idx"], x["q_scale"], x["w"])
-        nrm = 0.0
-        for t in sample_rows(spec.L, spec.topk, n=6, seed=4):
-            g = B.dsa_index_scores(qf, qs, x["k_idx"], x["k_scale"], row_begin=t, row_end=t + 1)
-            nrm = max(nrm, P.check_scores_row(to_np(g)[0], orc.scores_row(t), t))
-        say(f"score rows: worst normwise error {nrm:.3g}")
+    # indices that differ from the oracle's fp64 selection all lie inside the
+    # boundary window (checked per row above): longer rows hold more keys
+    # within fp32 accumulation error of their m-th score
+    say(f"rows={len(rows)} window-diffs={diffs} worst-attn={worst:.3g} worst score-row error={nrm:.3g}")
 
 
 @pytest.mark.parametrize("flags", [0, B.DSA_FLAG_FUSED], ids=["default", "fused"])
@@ -370,11 +371,16 @@ def test_forward_decode(dev, spec):
     gi = idx.cpu().numpy()
     off = n["offsets"]
     kv = x["kv"]
+    qf, qs = B.dsa_fold_index_query(x["q_idx"], x["q_scale"], x["w"])
     diffs = 0
     worst = 0.0
     for b in range(spec.B):
         sc = dec.scores_seq(b)
-        lo = int(off[b])
+        lo, hi = int(off[b]), int(off[b + 1])
+        # zero tolerance against the GPU's own fp32 scores of this sequence
+        gs = to_np(B.dsa_index_scores(qf[b:b + 1], qs[b:b + 1], x["k_idx"][lo:hi], x["k_scale"][lo:hi],
+                                      q_pos=torch.tensor([hi - lo - 1], dtype=torch.int64, device=dev)))[0]
+        assert np.array_equal(gi[b], od.pad_idx(od.topk_row(gs.astype(np.float64), spec.topk), spec.topk)), b
 
         def attend(sel, b=b, lo=lo):
             rows = od.as_f64(to_np(kv[lo + torch.as_tensor(np.asarray(sel, np.int64))]))
@@ -385,7 +391,6 @@ def test_forward_decode(dev, spec):
         diffs += d
         worst = max(worst, e)
     say(f"decode sequences={spec.B} window diffs={diffs} worst-attn={worst:.3g}")
-    assert diffs <= max(2, spec.B // 8)
 
 
 # ------------------------------------------------- fused indexer + select ---
