@@ -27,9 +27,12 @@
  *   - FP8 means OCP E4M3 ("e4m3fn": bias 7, max 448, NaN = S.1111.111) with
  *     one fp32 scale per row: value = e4m3(code) * scale[row].
  *   - Devices and threads: a call runs on the caller's current HIP device.
- *     The only global state is a per-device record of which kernels already
- *     have their LDS limit raised, updated atomically, so calls from several
- *     threads, on several streams or devices, may run concurrently.
+ *     The library's global state is per device and set once: whether the
+ *     device is gfx950 (checked on the first call), which kernels already
+ *     have their LDS limit raised, and the address of the device's copy of
+ *     the static scratch of dsa_forward_static.  Each record is updated
+ *     atomically, so calls from several threads, on several streams or
+ *     devices, may run concurrently (dsa_forward_static excepted: see there).
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -41,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 #define DSA_INDEX_DIM 128   /* index-key width, write-up section 2.2 */
 #define DSA_MAX_TOPK 4096
 
@@ -299,6 +302,30 @@ typedef struct dsa_forward_args {
 size_t dsa_forward_workspace_size(const dsa_forward_args* a);
 dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out, void* ws,
                          size_t ws_bytes, void* stream);
+
+/*
+ * dsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops (a decode
+ * step per token), harnesses that forbid allocation.  The call allocates
+ * nothing; its scratch memory is a static device array of
+ * DSA_STATIC_SCRATCH_BYTES (128 MiB) per device, part of the library's code
+ * object, held from the library's first use on that device until the process
+ * ends.  Results are those of dsa_forward with the same arguments (the same
+ * kernels run).
+ *
+ * Limit: the call needs what dsa_forward would take as its workspace (the
+ * indices count only when idx_out is NULL); above DSA_STATIC_SCRATCH_BYTES
+ * it returns DSA_ERR_WORKSPACE and launches nothing.  That covers a decode
+ * step of 64 sequences over caches of up to 131072 keys each (about 101 MiB)
+ * and short prefills; long prefills need dsa_forward.
+ *
+ * Every call on a device uses that device's one scratch array: calls whose
+ * work overlaps on one device (different streams, or host threads sharing a
+ * device) race and corrupt each other's results.  Calls on one stream, one
+ * after another, are safe.  Nothing in the scratch carries over between calls.
+ */
+#define DSA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+dsa_status_t dsa_forward_static(const dsa_forward_args* a, int32_t* idx_out, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,13 +25,14 @@ DSA_FLAG_FORCE_FALLBACK = 4
 DSA_FLAG_DYNAMIC_K = 8
 INDEX_DIM = 128
 MAX_TOPK = 4096
-ABI_VERSION = 5
+ABI_VERSION = 6
+STATIC_SCRATCH_BYTES = 128 << 20
 
 EXPORTED = [
     "dsa_abi_version", "dsa_status_str", "dsa_fold_index_query", "dsa_index_scores",
     "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_dynamic", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
     "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd", "dsa_indexer_kl_workspace_size", "dsa_indexer_kl",
-    "dsa_forward_workspace_size", "dsa_forward",
+    "dsa_forward_workspace_size", "dsa_forward", "dsa_forward_static",
 ]
 
 
@@ -81,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                             c_vp, c_vp, c_sz, c_vp], c_int),
         "dsa_forward_workspace_size": ([ctypes.POINTER(ForwardArgs)], c_sz),
         "dsa_forward": ([ctypes.POINTER(ForwardArgs), c_vp, c_vp, c_vp, c_sz, c_vp], c_int),
+        "dsa_forward_static": ([ctypes.POINTER(ForwardArgs), c_vp, c_vp, c_vp], c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -294,4 +296,12 @@ def dsa_forward(args: ForwardArgs, out, idx_out=None, ws=None, stream=None):
         ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=out.device)
     _check("dsa_forward", lib().dsa_forward(ctypes.byref(args), _p(idx_out), _p(out), _p(ws), ws.numel(),
                                             _stream(stream)))
+    return out, idx_out
+
+
+def dsa_forward_static(args: ForwardArgs, out, idx_out=None, stream=None):
+    """dsa_forward on the library's static scratch (no workspace, nothing
+    allocated by the call)."""
+    _check("dsa_forward_static", lib().dsa_forward_static(ctypes.byref(args), _p(idx_out), _p(out),
+                                                          _stream(stream)))
     return out, idx_out

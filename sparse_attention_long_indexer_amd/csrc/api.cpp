@@ -385,89 +385,152 @@ size_t dsa_forward_workspace_size(const dsa_forward_args* a) {
   return p.total + attn_workspace_bytes(a->attn_dtype == DSA_F32, a->T, a->H, a->Dv, a->topk);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The forward's launches once its arguments are validated, the device is
+// checked and `ws` holds at least forward_bytes(a, idx_out) bytes.
+dsa_status_t forward_run(const dsa_forward_args* a, int32_t* idx_out, void* out, void* ws, size_t ws_bytes,
+                         hipStream_t st) {
+  const FwdPlan p = plan_forward(a, idx_out == nullptr);
+  const size_t attn_ws = attn_workspace_bytes(a->attn_dtype == DSA_F32, a->T, a->H, a->Dv, a->topk);
+  char* base = (char*)ws;
+  void* qf = base + p.qf_off;
+  float* qs = (float*)(base + p.qs_off);
+  int32_t* idx = idx_out ? idx_out : (int32_t*)(base + p.idx_off);
+  float* sc = (float*)(base + p.sc_off);
+  const bool fp8 = a->idx_dtype == DSA_FP8_E4M3;
+  const int64_t R = a->T;
+  // the plan's regions follow one another inside the workspace
+  DSA_DEBUG_CHECK(p.qf_off + (size_t)R * 128 * (fp8 ? 1 : 4) <= p.qs_off);
+  DSA_DEBUG_CHECK(p.qs_off + (size_t)R * 4 <= p.idx_off);
+  DSA_DEBUG_CHECK(idx_out || p.idx_off + (size_t)R * (size_t)a->topk * 4 <= p.sc_off);
+  DSA_DEBUG_CHECK(!p.fused || p.sc_off + index_select_workspace_bytes(R, prefill_keys(a)) <= p.total);
+  DSA_DEBUG_CHECK(p.fused || a->mode != DSA_MODE_PREFILL ||
+                  (p.chunk_rows >= 1 && p.sc_off + (size_t)p.chunk_rows * (size_t)prefill_keys(a) * 4 <= p.total));
+  DSA_DEBUG_CHECK(a->mode != DSA_MODE_DECODE ||
+                  (p.sc_off + (size_t)a->total_keys * 4 <= p.topk_off && p.topk_off + p.topk_bytes <= p.total));
+  DSA_DEBUG_CHECK(p.total + attn_ws <= ws_bytes);
+  const DynK dyn = (a->flags & DSA_FLAG_DYNAMIC_K) ? DynK{a->dyn_theta, a->dyn_k_min} : kFixedK;
+
+  hipError_t e = launch_fold(a->q_idx, a->q_scale, fp8, a->w_index, a->w_dtype == DSA_BF16, R, qf,
+                             qs, st);
+  if (e != hipSuccess) return DSA_ERR_DEVICE;
+
+  AttnArgs at{};
+  at.q = a->q;
+  at.kv = a->kv;
+  at.v = a->v;
+  at.ld_kv = a->ld_kv;
+  at.ld_v = a->ld_v;
+  at.idx = idx;
+  at.T = R;
+  at.H = a->H;
+  at.Dk = a->Dk;
+  at.Dv = a->Dv;
+  at.k = a->topk;
+  at.scale = a->scale;
+  at.out = out;
+  at.lse = nullptr;
+
+  if (p.fused) {
+    const int64_t S = prefill_keys(a);
+    e = launch_index_select((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale, R, S, a->topk, idx,
+                            sc, (a->flags & DSA_FLAG_FORCE_FALLBACK) != 0, st, dyn);
+    if (e != hipSuccess) return DSA_ERR_DEVICE;
+    at.seq_offsets = nullptr;
+    at.S = S;
+  } else if (a->mode == DSA_MODE_PREFILL) {
+    const int64_t S = prefill_keys(a);
+    for (int64_t r0 = 0; r0 < R; r0 += p.chunk_rows) {
+      const int64_t r1 = r0 + p.chunk_rows < R ? r0 + p.chunk_rows : R;
+      e = launch_index_scores(qf, qs, a->k_idx, a->k_scale, fp8, R, S, nullptr, a->q_offset, r0, r1, sc, S,
+                              st);
+      if (e != hipSuccess) return DSA_ERR_DEVICE;
+      TopkRows tr{sc, S, nullptr, nullptr, S, nullptr, r0, a->q_offset};
+      e = launch_topk(tr, r1 - r0, S, a->topk, idx + r0 * a->topk, nullptr, nullptr, st, dyn);
+      if (e != hipSuccess) return DSA_ERR_DEVICE;
+    }
+    at.seq_offsets = nullptr;
+    at.S = S;
+  } else {
+    e = launch_index_scores_decode((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale,
+                                   a->seq_offsets, R, a->max_len, sc, st);
+    if (e != hipSuccess) return DSA_ERR_DEVICE;
+    TopkRows tr{sc, 0, nullptr, nullptr, 0, a->seq_offsets, 0, 0};
+    e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, p.topk_bytes ? base + p.topk_off : nullptr, st,
+                    dyn);
+    if (e != hipSuccess) return DSA_ERR_DEVICE;
+    at.seq_offsets = a->seq_offsets;
+    at.S = a->total_keys;
+  }
+  return from_hip(launch_attn(at, a->attn_dtype == DSA_F32, base + p.total, attn_ws, st));
+}
+
+// the workspace bytes one forward call needs (indices in the workspace
+// only when idx_out is NULL)
+size_t forward_bytes(const dsa_forward_args* a, const int32_t* idx_out) {
+  return plan_forward(a, idx_out == nullptr).total +
+         attn_workspace_bytes(a->attn_dtype == DSA_F32, a->T, a->H, a->Dv, a->topk);
+}
+
+dsa_status_t check_forward_call(const dsa_forward_args* a, const void* out) {
+  DSA_TRY(check_forward(a));
+  if (a->T == 0) return DSA_OK;
+  if (!out) return DSA_ERR_NULL;
+  if (a->attn_dtype == DSA_BF16 && !aligned(out, 8)) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+// ---- the static scratch of dsa_forward_static ------------------------------
+// One array per device, allocated with the code object and held until the
+// process ends.  Host code never uses the array's name as an address: each
+// device's copy is looked up once (hipGetSymbolAddress, with that device
+// current) and that address is what the kernels receive.
+constexpr size_t kStaticScratchBytes = DSA_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) static unsigned char scratch[kStaticScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+dsa_status_t static_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // a racing first call on the same device looks up the same address
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSA_ERR_DEVICE;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 dsa_status_t dsa_forward(const dsa_forward_args* a, int32_t* idx_out, void* out, void* ws,
                          size_t ws_bytes, void* stream) {
   try {
-    DSA_TRY(check_forward(a));
+    DSA_TRY(check_forward_call(a, out));
     if (a->T == 0) return DSA_OK;
-    if (!out) return DSA_ERR_NULL;
-    if (a->attn_dtype == DSA_BF16 && !aligned(out, 8)) return DSA_ERR_SHAPE;
-    const FwdPlan p = plan_forward(a, idx_out == nullptr);
-    const size_t attn_ws = attn_workspace_bytes(a->attn_dtype == DSA_F32, a->T, a->H, a->Dv, a->topk);
-    if (!ws || !aligned(ws, kAlign) || ws_bytes < p.total + attn_ws) return DSA_ERR_WORKSPACE;
+    if (!ws || !aligned(ws, kAlign) || ws_bytes < forward_bytes(a, idx_out)) return DSA_ERR_WORKSPACE;
     DSA_TRY(check_device());
-    hipStream_t st = as_stream(stream);
-    char* base = (char*)ws;
-    void* qf = base + p.qf_off;
-    float* qs = (float*)(base + p.qs_off);
-    int32_t* idx = idx_out ? idx_out : (int32_t*)(base + p.idx_off);
-    float* sc = (float*)(base + p.sc_off);
-    const bool fp8 = a->idx_dtype == DSA_FP8_E4M3;
-    const int64_t R = a->T;
-    // the plan's regions follow one another inside the workspace
-    DSA_DEBUG_CHECK(p.qf_off + (size_t)R * 128 * (fp8 ? 1 : 4) <= p.qs_off);
-    DSA_DEBUG_CHECK(p.qs_off + (size_t)R * 4 <= p.idx_off);
-    DSA_DEBUG_CHECK(idx_out || p.idx_off + (size_t)R * (size_t)a->topk * 4 <= p.sc_off);
-    DSA_DEBUG_CHECK(!p.fused || p.sc_off + index_select_workspace_bytes(R, prefill_keys(a)) <= p.total);
-    DSA_DEBUG_CHECK(p.fused || a->mode != DSA_MODE_PREFILL ||
-                    (p.chunk_rows >= 1 && p.sc_off + (size_t)p.chunk_rows * (size_t)prefill_keys(a) * 4 <= p.total));
-    DSA_DEBUG_CHECK(a->mode != DSA_MODE_DECODE ||
-                    (p.sc_off + (size_t)a->total_keys * 4 <= p.topk_off && p.topk_off + p.topk_bytes <= p.total));
-    DSA_DEBUG_CHECK(p.total + attn_ws <= ws_bytes);
-    const DynK dyn = (a->flags & DSA_FLAG_DYNAMIC_K) ? DynK{a->dyn_theta, a->dyn_k_min} : kFixedK;
+    return forward_run(a, idx_out, out, ws, ws_bytes, as_stream(stream));
+  } catch (...) {
+    return DSA_ERR_DEVICE;
+  }
+}
 
-    hipError_t e = launch_fold(a->q_idx, a->q_scale, fp8, a->w_index, a->w_dtype == DSA_BF16, R, qf,
-                               qs, st);
-    if (e != hipSuccess) return DSA_ERR_DEVICE;
-
-    AttnArgs at{};
-    at.q = a->q;
-    at.kv = a->kv;
-    at.v = a->v;
-    at.ld_kv = a->ld_kv;
-    at.ld_v = a->ld_v;
-    at.idx = idx;
-    at.T = R;
-    at.H = a->H;
-    at.Dk = a->Dk;
-    at.Dv = a->Dv;
-    at.k = a->topk;
-    at.scale = a->scale;
-    at.out = out;
-    at.lse = nullptr;
-
-    if (p.fused) {
-      const int64_t S = prefill_keys(a);
-      e = launch_index_select((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale, R, S, a->topk, idx,
-                              sc, (a->flags & DSA_FLAG_FORCE_FALLBACK) != 0, st, dyn);
-      if (e != hipSuccess) return DSA_ERR_DEVICE;
-      at.seq_offsets = nullptr;
-      at.S = S;
-    } else if (a->mode == DSA_MODE_PREFILL) {
-      const int64_t S = prefill_keys(a);
-      for (int64_t r0 = 0; r0 < R; r0 += p.chunk_rows) {
-        const int64_t r1 = r0 + p.chunk_rows < R ? r0 + p.chunk_rows : R;
-        e = launch_index_scores(qf, qs, a->k_idx, a->k_scale, fp8, R, S, nullptr, a->q_offset, r0, r1, sc, S,
-                                st);
-        if (e != hipSuccess) return DSA_ERR_DEVICE;
-        TopkRows tr{sc, S, nullptr, nullptr, S, nullptr, r0, a->q_offset};
-        e = launch_topk(tr, r1 - r0, S, a->topk, idx + r0 * a->topk, nullptr, nullptr, st, dyn);
-        if (e != hipSuccess) return DSA_ERR_DEVICE;
-      }
-      at.seq_offsets = nullptr;
-      at.S = S;
-    } else {
-      e = launch_index_scores_decode((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale,
-                                     a->seq_offsets, R, a->max_len, sc, st);
-      if (e != hipSuccess) return DSA_ERR_DEVICE;
-      TopkRows tr{sc, 0, nullptr, nullptr, 0, a->seq_offsets, 0, 0};
-      e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, p.topk_bytes ? base + p.topk_off : nullptr, st,
-                      dyn);
-      if (e != hipSuccess) return DSA_ERR_DEVICE;
-      at.seq_offsets = a->seq_offsets;
-      at.S = a->total_keys;
-    }
-    return from_hip(launch_attn(at, a->attn_dtype == DSA_F32, base + p.total, attn_ws, st));
+dsa_status_t dsa_forward_static(const dsa_forward_args* a, int32_t* idx_out, void* out, void* stream) {
+  try {
+    DSA_TRY(check_forward_call(a, out));
+    if (a->T == 0) return DSA_OK;
+    if (forward_bytes(a, idx_out) > kStaticScratchBytes) return DSA_ERR_WORKSPACE;
+    DSA_TRY(check_device());
+    void* ws = nullptr;
+    DSA_TRY(static_scratch(&ws));
+    return forward_run(a, idx_out, out, ws, kStaticScratchBytes, as_stream(stream));
   } catch (...) {
     return DSA_ERR_DEVICE;
   }

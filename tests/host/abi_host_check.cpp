@@ -49,6 +49,11 @@ std::map<const void*, int>& lds_limits() {  // dynamic LDS opted in per kernel
   static std::map<const void*, int> m;
   return m;
 }
+std::map<const void*, size_t>& vars() {  // registered device variables and their sizes
+  static std::map<const void*, size_t> m;
+  return m;
+}
+int g_symbol_lookups = 0;
 constexpr int kMaxGrid[3] = {2147483647, 65536, 65536};
 constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr size_t kLdsDefault = 64 * 1024;
@@ -88,6 +93,17 @@ hipError_t hipLaunchKernel(const void* fn, dim3 grid, dim3 block, void**, size_t
     std::fprintf(stderr, "bad launch of %s: grid (%u, %u, %u) block (%u, %u, %u) lds %zu (limit %zu)\n",
                  name.c_str(), grid.x, grid.y, grid.z, block.x, block.y, block.z, lds, limit);
   }
+  return hipSuccess;
+}
+void __hipRegisterVar(void**, void* var, char*, const char* name, int, size_t size, int, int) {
+  vars()[var] = size;
+  (void)name;
+}
+// the device copy of a registered variable lives at a fake device address
+hipError_t hipGetSymbolAddress(void** dev_ptr, const void* symbol) {
+  if (!vars().count(symbol)) return hipErrorInvalidSymbol;
+  *dev_ptr = (void*)((uintptr_t)1 << 44);
+  ++g_symbol_lookups;
   return hipSuccess;
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }
@@ -470,12 +486,47 @@ void check_forward() {
                                                      b.q_scale = nullptr; b.k_scale = nullptr; b.w_dtype = DSA_F32; });
 }
 
+// dsa_forward_static: the same launches on the library's static scratch,
+// which is looked up once per device; above its size nothing is launched
+void check_forward_static() {
+  int32_t* idx = (int32_t*)dptr(11);
+  void* out = dptr(12);
+  EXPECT(vars().size() == 1 && vars().begin()->second == DSA_STATIC_SCRATCH_BYTES);
+  dsa_forward_args d = prefill_args(64, kAttnShapes[3], true, 2048, 0, 0);
+  d.mode = DSA_MODE_DECODE;
+  d.seq_offsets = (const int64_t*)dptr(13);
+  d.total_keys = (int64_t)64 * 131072;
+  d.max_len = 131072;
+  const int lookups = g_symbol_lookups;
+  CALL(DSA_OK, true, dsa_forward_static(&d, idx, out, nullptr));
+  CALL(DSA_OK, true, dsa_forward_static(&d, nullptr, out, nullptr));
+  EXPECT(g_symbol_lookups == lookups + 1 || (lookups > 0 && g_symbol_lookups == lookups));
+  EXPECT(dsa_forward_workspace_size(&d) <= DSA_STATIC_SCRATCH_BYTES);
+  dsa_forward_args p = prefill_args(1000, kAttnShapes[3], true, 256, 0, 0);
+  CALL(DSA_OK, true, dsa_forward_static(&p, idx, out, nullptr));
+  dsa_forward_args big = prefill_args(6000, kAttnShapes[3], true, 2048, 0, 0);
+  EXPECT(dsa_forward_workspace_size(&big) > DSA_STATIC_SCRATCH_BYTES);
+  CALL(DSA_ERR_WORKSPACE, false, dsa_forward_static(&big, idx, out, nullptr));
+  d.total_keys = (int64_t)64 * 600000;  // scores of every cached key do not fit
+  d.max_len = 600000;
+  CALL(DSA_ERR_WORKSPACE, false, dsa_forward_static(&d, idx, out, nullptr));
+  CALL(DSA_ERR_NULL, false, dsa_forward_static(&p, idx, nullptr, nullptr));
+  CALL(DSA_ERR_NULL, false, dsa_forward_static(nullptr, idx, out, nullptr));
+  dsa_forward_args e = p;
+  e.T = 0;
+  CALL(DSA_OK, false, dsa_forward_static(&e, nullptr, nullptr, nullptr));
+}
+
 // a device that is not gfx950 is refused before anything is launched
 void check_other_device() {
   g_device = 1;
   void *q = dptr(3), *w = dptr(4), *o = dptr(5);
   float *qs = (float*)dptr(6), *os = (float*)dptr(7);
   CALL(DSA_ERR_DEVICE, false, dsa_fold_index_query(q, qs, DSA_FP8_E4M3, w, DSA_BF16, 8, o, os, nullptr));
+  {
+    dsa_forward_args p = prefill_args(1000, kAttnShapes[3], true, 256, 0, 0);
+    CALL(DSA_ERR_DEVICE, false, dsa_forward_static(&p, (int32_t*)dptr(11), dptr(12), nullptr));
+  }
   {
     dsa_forward_args a = prefill_args(100, kAttnShapes[3], true, 2048, 0, 0);
     const size_t ws = dsa_forward_workspace_size(&a);
@@ -495,6 +546,7 @@ int main() {
   check_bwd();
   check_kl();
   check_forward();
+  check_forward_static();
   check_other_device();
   std::printf("abi host check: %d checks, %d launches recorded, %d failures\n", g_checks, g_launches, g_failures);
   return g_failures == 0 ? 0 : 1;

@@ -56,7 +56,7 @@ def test_probe_library_exports(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.dsa_abi_version() == 5
+    assert lib.dsa_abi_version() == 6
     for s in range(7):
         assert lib.dsa_status_str(s)
     assert lib.dsa_status_str(99) == b"unknown status"
