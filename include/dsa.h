@@ -246,7 +246,10 @@ dsa_status_t dsa_indexer_kl(const float* q_idx, const float* k_idx, const float*
                             void* stream);
 
 /*
- * Whole forward: fold, scores, top-k and sparse attention.
+ * Whole forward: fold, scores, top-k and sparse attention -- the path of the
+ * write-up's sections 2.1-2.3 and 3.1: the lightning indexer scores every
+ * causal pair (2.2), the fine-grained selection keeps each query's k best
+ * keys (2.3), and attention in MLA's MQA mode runs over those keys (3.1).
  *
  * PREFILL: T query tokens at positions q_offset .. q_offset + T - 1 of one
  *   causal sequence whose first S = q_offset + T tokens are the keys

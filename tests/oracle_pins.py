@@ -381,6 +381,35 @@ def pin_attend_special_cases(od, oc):
     assert np.allclose(l1 - l0, 0.7 * 2.5, rtol=1e-12)
 
 
+def pin_attend_online_softmax(od, oc):
+    """The oracle's two-pass softmax attention equals the streaming form the
+    GPU kernels use (tiles of keys, a running maximum m and sum l, earlier
+    partial outputs rescaled by exp(m_old - m_new)): an algebraic identity,
+    checked in fp64 with tile sizes that leave a ragged last tile, and with a
+    later tile that raises the maximum by far more than the first."""
+    rng = np.random.default_rng(17)
+    H, n, Dk, Dv, scale = 5, 77, 24, 16, 0.4
+    q = rng.standard_normal((H, Dk))
+    k = rng.standard_normal((n, Dk))
+    k[50:] *= 6.0                       # the running maximum jumps mid-row
+    v = rng.standard_normal((n, Dv))
+    o_ref, lse_ref = od.attend(q, k, v, scale)
+    for tile in (1, 8, 32, 77):
+        m = np.full(H, -np.inf)
+        ls = np.zeros(H)
+        acc = np.zeros((H, Dv))
+        for j0 in range(0, n, tile):
+            z = scale * (q @ k[j0:j0 + tile].T)
+            m_new = np.maximum(m, z.max(axis=1))
+            r = np.exp(m - m_new)
+            e = np.exp(z - m_new[:, None])
+            ls = ls * r + e.sum(axis=1)
+            acc = acc * r[:, None] + e @ v[j0:j0 + tile]
+            m = m_new
+        assert np.allclose(acc / ls[:, None], o_ref, rtol=1e-12, atol=1e-13), tile
+        assert np.allclose(m + np.log(ls), lse_ref, rtol=1e-13, atol=1e-13), tile
+
+
 def pin_sparse_equals_dense(od, oc):
     """With k >= t+1 every key is kept and sparse attention equals dense
     causal attention (torch SDPA, float64, an independent routine)."""
@@ -564,7 +593,7 @@ ALL_PINS = [
     pin_e4m3_encode_midpoints_and_saturation, pin_bf16_decode_matches_library, pin_fold_orientation,
     pin_requant_closed_forms, pin_scores_one_hot, pin_brute_force, pin_prefill_chunk_brute_force,
     pin_scores_causal_relu, pin_topk_properties, pin_dynamic_k,
-    pin_attend_special_cases, pin_sparse_equals_dense, pin_decode_equals_prefill_row, pin_page_constants,
+    pin_attend_special_cases, pin_attend_online_softmax, pin_sparse_equals_dense, pin_decode_equals_prefill_row, pin_page_constants,
     pin_attend_backward_autograd_and_differences, pin_sparse_attn_backward_scatter,
     pin_indexer_kl_autograd, pin_indexer_kl_differences,
 ]
