@@ -351,25 +351,113 @@ inline int64_t filter_items(int64_t T, int64_t S) {
   return nb + (nb > first_long ? nb - first_long : 0);
 }
 
-__global__ __launch_bounds__(256, 2) void idx_filter_kernel(
+// A block has kFiltWaves compute waves (64 query rows each) and one producer
+// wave that alone moves key tiles into LDS (direct-to-LDS copies, three
+// buffers, two tiles in flight) and waits for them; tiles are handed over
+// with LDS-only barriers, so the compute waves never wait on their own
+// global stores.
+//
+// Survivors leave the MFMA loop in two steps, so that the per-score work is
+// a multiply and a third of a compare:
+//  1. a lane's four scores of one MFMA result (one query, keys 4g .. 4g+3 of
+//     a 16-key group) pass as a group when their maximum reaches the row's
+//     threshold; passing groups take consecutive slots of the wave's LDS
+//     ring (ballot + mbcnt): the four scores and a tag naming row and keys;
+//  2. whenever the ring holds 64 groups, one flush round gives each lane a
+//     group: it keeps the scores that pass exactly (threshold and causal
+//     position), takes their places in the row's segment with one LDS
+//     atomic, and stores them; a round's stores are 64 lanes wide.
+// The four 16-key groups of every aligned 64-key block go to the row's four
+// segments in an order rotated by a hash of the block: a row that keeps
+// every key fills its segments evenly, and periodic key patterns (one
+// planted key per 64) spread over all four.
+constexpr int kFiltWaves = kFiltRows / 64;
+constexpr int kFiltThreads = (kFiltWaves + 1) * 64;
+constexpr int kFiltBufs = 3;
+constexpr int kRing = 256;      // group slots per compute wave's ring
+constexpr int kTileCopies = 9;  // copies per key tile: 8 of key bytes, 1 of scales
+
+__device__ __forceinline__ int seg_of(uint32_t koff) {
+  return (int)(((koff >> 4) + (((koff >> 6) * 0x9E3779B1u) >> 30)) & 3u);
+}
+
+__global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, int64_t T, int64_t S, const float* __restrict__ tau,
     uint2* __restrict__ cand, int32_t* __restrict__ cnt_out) {
-  __shared__ __align__(16) uint8_t ktile[2][kFiltKeys * kIdxDim];
-  __shared__ __align__(16) float kst[2][kFiltKeys];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ __align__(16) uint8_t ktile[kFiltBufs][kFiltKeys * kIdxDim];
+  __shared__ __align__(16) float kst[kFiltBufs][kFiltKeys];
+  __shared__ __align__(16) v4f vring[kFiltWaves][kRing];     // a group's four scores
+  __shared__ uint32_t tring[kFiltWaves][kRing];              // ... and its tag
+  __shared__ uint32_t rcnt[kFiltWaves][64 * kSeg];           // per (row of the wave, segment)
+  __shared__ float tvtab[kFiltWaves][64];                    // per row: survivor threshold on v
+  __shared__ int tqtab[kFiltWaves][64];                      // ... and the last key it sees
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const FilterItem item = filter_item(blockIdx.x, T, S);
+  const int ntiles = (int)((item.k1 - item.k0 + kFiltKeys - 1) / kFiltKeys);
+
+  if (w == kFiltWaves) {
+    // producer: tile j's 64 keys x 128 B = 512 16-byte chunks (8 per lane),
+    // stored fragment-major: copy i = 2 kt + h puts, at LDS byte 1024 i +
+    // 16 l, the 16 bytes lane l = (g, c) supplies as half h of its A operand
+    // for key subtile kt (key kb + 16 kt + c, bytes 32 g + 16 h), so every
+    // operand read is lane-linear (bank-conflict free); then one scale per
+    // lane.  Keys past S are clamped to key S - 1 (the causal mask drops
+    // them), so every tile is exactly kTileCopies copies and the memory
+    // counter tells which tiles have landed.
+    auto issue = [&](int it) {
+      const int buf = it % kFiltBufs;
+      const int64_t kb = item.k0 + (int64_t)it * kFiltKeys;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kt = i >> 1, h = i & 1;
+        const int64_t key = min(kb + 16 * kt + c, S - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(k8 + key * kIdxDim + 32 * g + 16 * h),
+            (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint8_t*)ktile[buf] +
+                                                      i * 1024),
+            16, 0, 0);
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(ks + min(kb + lane, S - 1)),
+          (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)kst[buf]), 4, 0, 0);
+    };
+    // s_waitcnt vmcnt(kTileCopies): all but the last tile issued have landed
+    constexpr int kWaitOneTile = 0x3F70 | (kTileCopies & 15) | ((kTileCopies >> 4) << 14);
+    if (ntiles > 0) issue(0);
+    if (ntiles > 1) {
+      issue(1);
+      __builtin_amdgcn_s_waitcnt(kWaitOneTile);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __builtin_amdgcn_s_barrier();
+    // barrier it + 1 hands over tile it + 1 (the consumers are done reading
+    // tile it - 1, whose buffer tile it + 2 reuses)
+    for (int it = 0; it + 1 < ntiles; ++it) {
+      if (it + 2 < ntiles) {
+        issue(it + 2);
+        __builtin_amdgcn_s_waitcnt(kWaitOneTile);
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __builtin_amdgcn_s_barrier();
+    }
+    return;
+  }
+
   const int64_t R0 = item.rb * kFiltRows;
   const int64_t Q0 = R0 + 64 * w;   // the wave's first row
-  const int64_t P0 = S - T + Q0;    // ... and its position
+  v4f* const vr = vring[w];
+  uint32_t* const tr = tring[w];
+  uint32_t* const rc = rcnt[w];
+#pragma unroll
+  for (int i = 0; i < kSeg; ++i) rc[i * 64 + lane] = 0u;
 
   v8i bq[4];
   int tq[4];
   float tv[4];
-  uint32_t cnt[4];
-  bool ovf[4];
-  uint2* seg[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t t = Q0 + 16 * q + c;
@@ -381,107 +469,131 @@ __global__ __launch_bounds__(256, 2) void idx_filter_kernel(
     // survivors need v * qs >= tau; shave a few ulps so rounding of the
     // product can never drop a key whose final score reaches tau
     tv[q] = !ok ? INFINITY : ta == -INFINITY ? -INFINITY : (ta / qs[tt]) * (1.0f - 1.0f / (1 << 20));
-    cnt[q] = 0;
-    ovf[q] = false;
-    seg[q] = cand + ((tt * kSets + item.set) * kSeg + g) * (int64_t)kSegStride;
   }
-  const int ntiles = (int)((item.k1 - item.k0 + kFiltKeys - 1) / kFiltKeys);
-
-  // tile loader: 64 keys x 128 B = 512 chunks (2 per thread) + 64 scales
-  auto issue = [&](int it, int buf) {
-    const int64_t kb = item.k0 + (int64_t)it * kFiltKeys;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int chunk = (i * 4 + w) * 64 + lane;       // 16-byte chunk of the tile
-      const int64_t key = min(kb + (chunk >> 3), S - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(k8 + key * kIdxDim + (chunk & 7) * 16),
-          (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint8_t*)ktile[buf] +
-                                                    (i * 4 + w) * 1024),
-          16, 0, 0);
-    }
-    // scales: lanes 0..15 of wave 0 fetch 4 each; a group running past S is
-    // filled by hand in the last tile
-    if (w == 0 && lane < 16 && kb + 4 * lane + 3 < S) {
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(ks + kb + 4 * lane),
-          (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)kst[buf]), 16, 0, 0);
-    }
-  };
-  if (ntiles > 0) issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int64_t kb = item.k0 + (int64_t)it * kFiltKeys;
-    if (it + 1 < ntiles) issue(it + 1, buf ^ 1);
-    if (kb + kFiltKeys > S) {  // partial last tile: fill its scales by hand
-      for (int i = threadIdx.x; i < kFiltKeys; i += 256) {
-        const int64_t key = kb + i;
-        if ((key & ~3LL) + 3 >= S) kst[buf][i] = key < S ? ks[key] : 0.f;
-      }
-      __syncthreads();
-    }
-    // a segment grows by at most 16 per tile: clamp once per tile into the
-    // sink slots past kCap and remember the overflow
+  if (g == 0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (cnt[q] > (uint32_t)kCap) {
-        ovf[q] = true;
-        cnt[q] = kCap;
-      }
+      tvtab[w][16 * q + c] = tv[q];
+      tqtab[w][16 * q + c] = tq[q];
     }
-    const bool mask = kb + kFiltKeys - 1 > P0;  // some key may lie past a query of this wave
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int k16 = (int)(kb + 16 * kt);
-      const int rot = tile_rot(k16 >> 4);
-      const int ar = (c + rot) & 15;                  // A row c holds key k16 + ar
-      const v8i a = *(const v8i*)(ktile[buf] + (16 * kt + ar) * kIdxDim + 32 * g);
-      v4f acc[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = mfma_fp8_16x16x128(a, bq[q], (v4f){0.f, 0.f, 0.f, 0.f});
-      int key[4];
-      float kss[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kr = (4 * g + i + rot) & 15;        // C row 4g+i holds key k16 + kr
-        key[i] = k16 + kr;
-        kss[i] = kst[buf][16 * kt + kr];
-      }
-      if (mask) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = acc[q][i] * kss[i];
-            const bool pass = (v >= tv[q]) & (key[i] <= tq[q]);
-            if (pass) seg[q][cnt[q]] = make_uint2(__float_as_uint(v), (uint32_t)key[i]);
-            cnt[q] += pass ? 1u : 0u;
-          }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = acc[q][i] * kss[i];
-            const bool pass = v >= tv[q];
-            if (pass) seg[q][cnt[q]] = make_uint2(__float_as_uint(v), (uint32_t)key[i]);
-            cnt[q] += pass ? 1u : 0u;
-          }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
+  // tag of a group: key offset of its first key from the item's first key
+  // << 6, then the row within the wave (16 q + c)
+  const uint32_t lane_tag = (uint32_t)((4 * g) << 6) | (uint32_t)c;
+  uint32_t ptr = 0, tail = 0;   // ring write and flush positions (wave-uniform)
+
+  // one flush round: up to 64 ring groups, one per lane
+  uint2* const wave_seg = cand + (Q0 * kSets + item.set) * kSeg * (int64_t)kSegStride;
+  auto flush = [&](uint32_t n) {
+    const v4f vv = vr[tail + lane];
+    const uint32_t tag = tr[tail + lane];
+    const int rl = (int)(tag & 63u);
+    const uint32_t koff = tag >> 6;
+    const int sg = seg_of(koff);
+    const float tvr = tvtab[w][rl];
+    const int tqr = tqtab[w][rl];
+    const int key0 = (int)(item.k0 + koff);
+    const bool live = (uint32_t)lane < n;
+    bool p[4];
+    uint32_t np = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = live & (vv[i] >= tvr) & (key0 + i <= tqr);
+      np += p[i] ? 1u : 0u;
+    }
+    uint32_t r = 0;
+    if (np) r = atomicAdd(&rc[sg * 64 + rl], np);
+    // segment (row Q0 + rl, this item's key chunk, sg) within the wave's rows
+    uint2* const dst = wave_seg + (uint32_t)(rl * (kSets * kSeg) + sg) * (uint32_t)kSegStride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (p[i] && r < (uint32_t)kCap) dst[r] = make_uint2(__float_as_uint(vv[i]), (uint32_t)(key0 + i));
+      r += p[i] ? 1u : 0u;
+    }
+    tail += n;
+  };
+
+  // groups of one 16-key step (kt) of a tile: four MFMA results, one per
+  // query group q, four scores per lane
+  auto epilogue = [&](const v4f (&acc)[4], const v4f& kss, uint32_t step_tag) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f v = {acc[q][0] * kss[0], acc[q][1] * kss[1], acc[q][2] * kss[2], acc[q][3] * kss[3]};
+      const bool pass = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) >= tv[q];
+      const uint64_t m = ballot(pass);
+      if (pass) {
+        // wave-uniform bases, the lane's rank among the passing lanes
+        v4f* const vb = vr + ptr;
+        uint32_t* const tb = tr + ptr;
+        const uint32_t rank = lanes_below(m);
+        vb[rank] = v;
+        tb[rank] = step_tag + (uint32_t)(16 * q);
+      }
+      ptr += (uint32_t)__popcll(m);
+      // at most 64 new groups per step: one round brings the ring below 64;
+      // when the next step might run past its end, the (< 64) live groups
+      // move to its front
+      if (ptr - tail >= 64u) flush(64u);
+      if (ptr > (uint32_t)(kRing - 64)) {
+        const uint32_t nl = ptr - tail;
+        const v4f e = vr[tail + lane];
+        const uint32_t et = tr[tail + lane];
+        __builtin_amdgcn_wave_barrier();
+        if ((uint32_t)lane < nl) {
+          vr[lane] = e;
+          tr[lane] = et;
+        }
+        __builtin_amdgcn_wave_barrier();
+        tail = 0;
+        ptr = nl;
+      }
+    }
+  };
+  // one step's MFMAs: A row c (key kb + 16 kt + c), bytes 32 g .. 32 g + 31,
+  // in two lane-linear reads; the key scales of C rows 4g .. 4g+3
+  auto mfmas = [&](int buf, int kt, v4f (&acc)[4], v4f& kss) {
+    const v4i a0 = *(const v4i*)(ktile[buf] + (2 * kt) * 1024 + 16 * lane);
+    const v4i a1 = *(const v4i*)(ktile[buf] + (2 * kt + 1) * 1024 + 16 * lane);
+    const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    kss = *(const v4f*)(&kst[buf][16 * kt + 4 * g]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = mfma_fp8_16x16x128(a, bq[q], (v4f){0.f, 0.f, 0.f, 0.f});
+  };
+
+  // software pipeline over the four 16-key steps of each tile, two sets of
+  // accumulators in turn: the MFMAs of step s + 1 are issued before the
+  // epilogue of step s; the barrier that hands over the next tile sits
+  // between the last read of one tile and the first of the next (the
+  // epilogue only reads registers and the wave's own ring)
+  lds_barrier();   // the producer's first tile
+  v4f acc_a[4], acc_b[4], kss_a, kss_b;
+  if (ntiles > 0) mfmas(0, 0, acc_a, kss_a);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it % kFiltBufs;
+    const uint32_t tag0 = ((uint32_t)(it * kFiltKeys) << 6) + lane_tag;
+    mfmas(buf, 1, acc_b, kss_b);
+    epilogue(acc_a, kss_a, tag0);
+    mfmas(buf, 2, acc_a, kss_a);
+    epilogue(acc_b, kss_b, tag0 + (16u << 6));
+    mfmas(buf, 3, acc_b, kss_b);
+    epilogue(acc_a, kss_a, tag0 + (32u << 6));
+    if (it + 1 < ntiles) {
+      lds_barrier();   // done with tile it; tile it + 1 has landed
+      mfmas((it + 1) % kFiltBufs, 0, acc_a, kss_a);
+    }
+    epilogue(acc_b, kss_b, tag0 + (48u << 6));
+  }
+  if (ptr != tail) flush(ptr - tail);
+
   const bool two = item.rb >= filter_first_long(T, S);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (tq[q] < 0) continue;
-    const int64_t t = Q0 + 16 * q + c;  // the row (tq holds its position)
-    const int v = (ovf[q] || cnt[q] > (uint32_t)kCap) ? kCap + 1 : (int)cnt[q];
-    cnt_out[(t * kSets + item.set) * kSeg + g] = v;
+    const int rl = 16 * q + c;
+    const int64_t t = Q0 + rl;
+    // lane group g reports segment g of its rows
+    const uint32_t n = rc[g * 64 + rl];
+    cnt_out[(t * kSets + item.set) * kSeg + g] = n > (uint32_t)kCap ? kCap + 1 : (int)n;
     if (!two) cnt_out[(t * kSets + 1) * kSeg + g] = 0;  // rows with one key chunk
   }
 }
@@ -712,7 +824,7 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
     idx_refine_kernel<<<(unsigned)((T + kRefRows - 1) / kRefRows), 256, 0, st>>>(qf, qs, k8, ks, T, S, topk, tau);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  idx_filter_kernel<<<(unsigned)filter_items(T, S), 256, 0, st>>>(qf, qs, k8, ks, T, S, tau, cand, cnt);
+  idx_filter_kernel<<<(unsigned)filter_items(T, S), kFiltThreads, 0, st>>>(qf, qs, k8, ks, T, S, tau, cand, cnt);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // bitmap words of the longest row with a bitmap, or the bucket pass's words
   const int64_t bn = S < kSelBitmapN ? S : kSelBitmapN;
