@@ -61,6 +61,12 @@ __device__ __forceinline__ int tile_rot(int64_t key16) {
 __global__ void zero_i32_kernel(int32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
+__global__ void zero_heads_kernel(int32_t* a, int32_t* b) {
+  if (threadIdx.x == 0) {
+    a[0] = 0;
+    b[0] = 0;
+  }
+}
 
 // ---- 1. threshold estimate ------------------------------------------------
 constexpr int kEstWaves = 16;
@@ -601,16 +607,286 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
 // ---- 3. exact select over survivors ---------------------------------------
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelMax = 6144;             // survivor slots a row may stage in LDS
+constexpr int kSelMax = 6144;             // survivor slots a row may hold
 constexpr int kChunk = 64;                // survivors per 512-byte direct-to-LDS copy
 constexpr int kMaxChunks = kSelMax / kChunk;
 constexpr int kMaxTies = 512;             // keys equal to the m-th best kept in a list
+constexpr int kGenericBlocks = 512;       // persistent grid of the generic select
 
-__global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
+// 3a. Fast path, one block per row.  Every thread holds up to kSfPer of the
+// row's survivors in registers (final score key, position).  One histogram
+// of kSfBins bins spanning [lo, hi] (lo = the key of the row's threshold,
+// or its smallest key when the row kept every key; hi = its largest key)
+// finds the bin b of the m-th best key.  Every key in a bin above b is kept;
+// the keys in b (at most kSfList) are ranked among themselves under (score
+// desc, position asc) and the first m - #(keys above b) of them are kept.
+// Kept positions are marked in a bitmap over the row's positions, whose
+// prefix popcounts give the ascending output.  Rows this path does not
+// settle go to a queue for the generic select (3b): a dynamic k, rows past
+// the bitmap length, m above kSfBins, a boundary bin fuller than kSfList.
+// Rows whose survivors cannot hold the answer (a segment past capacity,
+// more than kSelMax survivors, fewer than m survivors at the threshold) go
+// to the exact fallback (4).
+constexpr int kSfThreads = 512;
+constexpr int kSfWaves = kSfThreads / 64;
+constexpr int kSfPer = kSelMax / kSfThreads;
+constexpr int kSfBins = 2048;
+constexpr int kSfList = 512;
+static_assert(kSfPer * kSfThreads == kSelMax, "threads must divide the survivor slots");
+static_assert(kSfBins == 4 * kSfThreads, "the bin scan gives each thread four bins");
+
+__global__ __launch_bounds__(kSfThreads) void idx_select_fast_kernel(
     const float* __restrict__ qs, const float* __restrict__ tau, const uint2* __restrict__ cand,
     const int32_t* __restrict__ cnt_in, int64_t T, int64_t S, int64_t topk, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ fb, int force_fallback, DynK dyn) {
-  extern __shared__ __align__(16) uint32_t sm[];
+    int32_t* __restrict__ gq, int32_t* __restrict__ fb, int force_fallback, DynK dyn) {
+  extern __shared__ __align__(16) uint32_t bitmap[];  // [(n + 31) / 32] kept positions
+  __shared__ uint32_t hist[kSfBins];                   // bin counts, then the staged output
+  __shared__ uint32_t lkey[kSfList];
+  __shared__ int32_t lpos[kSfList];
+  __shared__ uint32_t red[4][kSfWaves];
+  __shared__ uint32_t s_bin, s_above, s_nlist;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t = blockIdx.x;
+  const int64_t n = min(S - T + t + 1, S);
+  const int64_t m = min(topk, n);
+  int32_t* o = idx_out + t * topk;
+  if (n <= topk && !dyn_on(dyn)) {  // every key is kept
+    for (int64_t i = tid; i < topk; i += kSfThreads) o[i] = i < n ? (int32_t)i : -1;
+    return;
+  }
+  auto defer = [&](int32_t* q) {
+    if (tid == 0) q[1 + atomicAdd(&q[0], 1)] = (int32_t)t;
+  };
+  if (force_fallback) {
+    defer(fb);
+    return;
+  }
+  if (dyn_on(dyn) || n > kSelBitmapN || m > kSfBins) {
+    defer(gq);
+    return;
+  }
+  // segment starts in the concatenation of the row's segments
+  int cb[kSets * kSeg + 1];
+  bool over = false;
+  cb[0] = 0;
+#pragma unroll
+  for (int g = 0; g < kSets * kSeg; ++g) {
+    const int c = cnt_in[t * kSets * kSeg + g];
+    over |= c > kCap;
+    cb[g + 1] = cb[g] + (c > kCap ? kCap : c);
+  }
+  const int total = cb[kSets * kSeg];
+  const float tt = tau[t];
+  if (over || total > kSelMax || (tt == -INFINITY && total != n)) {
+    defer(fb);
+    return;
+  }
+  // load: slot e = tid + kSfThreads j of the concatenation; final score
+  // u = v * qs with ReLU, as a score key
+  const float qsc = qs[t];
+  uint32_t key[kSfPer];
+  int32_t pos[kSfPer];
+#pragma unroll
+  for (int j = 0; j < kSfPer; ++j) {
+    const int e = tid + kSfThreads * j;
+    int g = 0, start = 0;
+#pragma unroll
+    for (int i = 1; i < kSets * kSeg; ++i)
+      if (e >= cb[i]) {
+        g = i;
+        start = cb[i];
+      }
+    uint2 cv = make_uint2(0u, 0xFFFFFFFFu);
+    if (e < total) cv = cand[(t * kSets * kSeg + g) * (int64_t)kSegStride + (e - start)];
+    const float u0 = __uint_as_float(cv.x) * qsc;
+    const bool ok = e < total && (int32_t)cv.y >= 0 && (int64_t)(int32_t)cv.y < n;
+    key[j] = ok ? score_key(u0 > 0.f ? u0 : 0.f) : 0u;   // 0 is below every real key
+    pos[j] = ok ? (int32_t)cv.y : -1;
+  }
+  // range of the keys and the count at or above the threshold; a row that
+  // kept every key is ranked over its positive scores (lo = its smallest
+  // positive key) when at least m of them are positive
+  const uint32_t lo_t = tt != -INFINITY ? score_key(tt) : kZeroKey + 1u;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu, nge = 0u;
+#pragma unroll
+  for (int j = 0; j < kSfPer; ++j) {
+    if (pos[j] >= 0) {
+      mx = max(mx, key[j]);
+      nge += key[j] >= lo_t ? 1u : 0u;
+      if (key[j] >= lo_t) mn = min(mn, key[j]);
+    }
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  nge = wave_sum_u32(nge);
+  if (lane == 0) {
+    red[0][w] = mx;
+    red[1][w] = mn;
+    red[2][w] = nge;
+  }
+  const int nwords = (int)((n + 127) >> 7) * 4;   // whole 16-byte groups
+  for (int i = tid; i < kSfBins; i += kSfThreads) hist[i] = 0u;
+  for (int i = tid; i < nwords; i += kSfThreads) bitmap[i] = 0u;
+  if (tid == 0) s_nlist = 0u;
+  __syncthreads();
+  mx = 0u;
+  mn = 0xFFFFFFFFu;
+  nge = 0u;
+#pragma unroll
+  for (int i = 0; i < kSfWaves; ++i) {
+    mx = max(mx, red[0][i]);
+    mn = min(mn, red[1][i]);
+    nge += red[2][i];
+  }
+  // survivors at the threshold must hold the m best
+  if (tt != -INFINITY && nge < (uint32_t)m) {
+    defer(fb);
+    return;
+  }
+  const int ngrp = nwords >> 2;
+  const int per = (ngrp + kSfThreads - 1) / kSfThreads;
+  const int g0 = tid * per, g1 = min(ngrp, g0 + per);
+  uint4* const bm4 = (uint4*)bitmap;
+  if (nge < (uint32_t)m) {
+    // a row that kept every key with fewer than m positive scores: every
+    // positive score is kept, and the m - nge lowest positions scoring zero
+#pragma unroll
+    for (int j = 0; j < kSfPer; ++j)
+      if (pos[j] >= 0 && key[j] >= lo_t) atomicOr(&bitmap[pos[j] >> 5], 1u << (pos[j] & 31));
+    __syncthreads();
+    // zeros (unset positions below n) per run of groups, then their prefix
+    uint32_t z = 0u;
+    for (int i = g0; i < g1; ++i) {
+      const uint4 q = bm4[i];
+      const int64_t b0 = (int64_t)i * 128;
+      const uint32_t valid = (uint32_t)(n - b0 >= 128 ? 128 : (n > b0 ? n - b0 : 0));
+      z += valid - (uint32_t)(__popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w));
+    }
+    const uint32_t zincl = wave_incl_scan(z);
+    if (lane == 63) red[3][w] = zincl;
+    __syncthreads();
+    uint32_t zr = zincl - z;
+#pragma unroll
+    for (int i = 0; i < kSfWaves; ++i) zr += i < w ? red[3][i] : 0u;
+    const uint32_t need0 = (uint32_t)m - nge;
+    for (int i = g0; i < g1 && zr < need0; ++i) {
+      for (int e = 0; e < 4 && zr < need0; ++e) {
+        const int wi = 4 * i + e;
+        const int64_t b0 = (int64_t)wi * 32;
+        const uint32_t inrow = n - b0 >= 32 ? 0xFFFFFFFFu : (n > b0 ? (1u << (n - b0)) - 1u : 0u);
+        uint32_t zb = ~bitmap[wi] & inrow, keep = 0u;
+        while (zb && zr < need0) {
+          const uint32_t bit = zb & (0u - zb);
+          keep |= bit;
+          ++zr;
+          zb ^= bit;
+        }
+        bitmap[wi] |= keep;   // this thread alone owns word wi
+      }
+    }
+    __syncthreads();
+  } else {
+    const uint32_t lo = tt != -INFINITY ? lo_t : mn;
+    const uint32_t span = mx - lo;
+    const int top = span ? 31 - __builtin_clz(span) : 0;
+    const int sh = top > 10 ? top - 10 : 0;   // (span >> sh) < kSfBins
+#pragma unroll
+    for (int j = 0; j < kSfPer; ++j)
+      if (pos[j] >= 0 && key[j] >= lo) atomicAdd(&hist[(key[j] - lo) >> sh], 1u);
+    __syncthreads();
+    // bin of the m-th best: descending scan, thread tid owns bins
+    // kSfBins - 1 - 4 tid - e
+    uint32_t c4[4], own = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c4[e] = hist[kSfBins - 1 - 4 * tid - e];
+      own += c4[e];
+    }
+    uint32_t incl = wave_incl_scan(own);
+    if (lane == 63) red[3][w] = incl;
+    __syncthreads();
+    uint32_t above = incl - own;
+#pragma unroll
+    for (int i = 0; i < kSfWaves; ++i) above += i < w ? red[3][i] : 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (above < (uint32_t)m && (uint32_t)m <= above + c4[e]) {
+        s_bin = (uint32_t)(kSfBins - 1 - 4 * tid - e);
+        s_above = above;
+      }
+      above += c4[e];
+    }
+    __syncthreads();
+    const uint32_t bb = s_bin, remaining = (uint32_t)m - s_above, nl = hist[bb];
+    if (nl > (uint32_t)kSfList) {
+      defer(gq);
+      return;
+    }
+    // keys above the boundary bin are kept; the boundary bin goes to the list
+#pragma unroll
+    for (int j = 0; j < kSfPer; ++j) {
+      if (pos[j] < 0 || key[j] < lo) continue;
+      const uint32_t b = (key[j] - lo) >> sh;
+      if (b > bb) {
+        atomicOr(&bitmap[pos[j] >> 5], 1u << (pos[j] & 31));
+      } else if (b == bb) {
+        const uint32_t i = atomicAdd(&s_nlist, 1u);
+        lkey[i] = key[j];
+        lpos[i] = pos[j];
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < (int)nl; i += kSfThreads) {
+      const uint32_t ki = lkey[i];
+      const int32_t pi = lpos[i];
+      uint32_t r = 0u;
+      for (int j = 0; j < (int)nl; ++j) {
+        const uint32_t kj = lkey[j];
+        r += (kj > ki || (kj == ki && lpos[j] < pi)) ? 1u : 0u;
+      }
+      if (r < remaining) atomicOr(&bitmap[pi >> 5], 1u << (pi & 31));
+    }
+    __syncthreads();
+  }
+  // ascending output: prefix popcounts over runs of `per` 16-byte groups per
+  // thread, staged in hist (m <= kSfBins) for one coalesced copy
+  uint32_t mine = 0u;
+  for (int i = g0; i < g1; ++i) {
+    const uint4 q = bm4[i];
+    mine += __popc(q.x) + __popc(q.y) + __popc(q.z) + __popc(q.w);
+  }
+  const uint32_t incl = wave_incl_scan(mine);
+  if (lane == 63) red[0][w] = incl;
+  __syncthreads();
+  uint32_t at = incl - mine;
+#pragma unroll
+  for (int i = 0; i < kSfWaves; ++i) at += i < w ? red[0][i] : 0u;
+  for (int i = g0; i < g1; ++i) {
+    const uint4 q = bm4[i];
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t wv = qw[e];
+      while (wv) {
+        const int b = __builtin_ctz(wv);
+        if (at < (uint32_t)m) hist[at] = (uint32_t)((4 * i + e) * 32 + b);
+        ++at;
+        wv &= wv - 1;
+      }
+    }
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < topk; i += kSfThreads) o[i] = i < m ? (int32_t)hist[i] : -1;
+}
+
+// 3b. Generic select for the rows the fast path queued: the survivors are
+// staged in LDS, a radix select over them finds the m-th best (and a
+// dynamic k's budget), and the output goes through a bitmap (or buckets for
+// rows past the bitmap length).  A persistent grid walks the queue.
+__device__ inline void select_generic_row(
+    int64_t t, uint32_t* sm, const float* __restrict__ qs, const float* __restrict__ tau,
+    const uint2* __restrict__ cand, const int32_t* __restrict__ cnt_in, int64_t T, int64_t S, int64_t topk,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ fb, DynK dyn) {
   uint2* cl = (uint2*)sm;                       // [kSelMax] (score key, position) pairs
   uint32_t* sel = sm + 2 * kSelMax;             // [nwords] bitmap of kept positions (or a long row's buckets)
   __shared__ uint32_t hist[1024];
@@ -620,7 +896,6 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   __shared__ int32_t s_tie[kMaxTies];
   __shared__ int s_ntie, s_bad;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t t = blockIdx.x;
   const int64_t n = min(S - T + t + 1, S);
   int64_t m = min(topk, n);
   int32_t* o = idx_out + t * topk;
@@ -651,7 +926,7 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
     s_bad = bad || nch > kMaxChunks || (tt == -INFINITY && total != n);
   }
   __syncthreads();
-  if (s_bad || force_fallback) {
+  if (s_bad) {
     if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
     return;
   }
@@ -750,6 +1025,18 @@ __global__ __launch_bounds__(kSelThreads) void idx_select_kernel(
   }
 }
 
+__global__ __launch_bounds__(kSelThreads) void idx_select_generic_kernel(
+    const float* __restrict__ qs, const float* __restrict__ tau, const uint2* __restrict__ cand,
+    const int32_t* __restrict__ cnt_in, int64_t T, int64_t S, int64_t topk, int32_t* __restrict__ idx_out,
+    const int32_t* __restrict__ gq, int32_t* __restrict__ fb, DynK dyn) {
+  extern __shared__ __align__(16) uint32_t sm[];
+  const int nq = gq[0];
+  for (int f = blockIdx.x; f < nq; f += gridDim.x) {
+    select_generic_row(gq[1 + f], sm, qs, tau, cand, cnt_in, T, S, topk, idx_out, fb, dyn);
+    __syncthreads();   // LDS is reused by the next row
+  }
+}
+
 // ---- 4. exact fallback for rows the survivors cannot settle ---------------
 constexpr int kFbBlocks = 64;
 
@@ -792,6 +1079,7 @@ size_t index_select_workspace_bytes(int64_t T, int64_t S) {
   add((size_t)T * kSets * kSeg * kSegStride * 8 + kChunk * 8);  // survivors (+ copy overrun pad)
   add((size_t)T * kSets * kSeg * 4);                // counts
   add((size_t)(T + 1) * 4);                 // fallback queue
+  add((size_t)(T + 1) * 4);                 // generic-select queue
   add((size_t)kFbBlocks * S * 4);           // fallback score rows
   return b;
 }
@@ -812,10 +1100,11 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
   uint2* cand = (uint2*)take((size_t)T * kSets * kSeg * kSegStride * 8 + kChunk * 8);
   int32_t* cnt = (int32_t*)take((size_t)T * kSets * kSeg * 4);
   int32_t* fb = (int32_t*)take((size_t)(T + 1) * 4);
+  int32_t* gq = (int32_t*)take((size_t)(T + 1) * 4);
   float* scratch = (float*)take((size_t)kFbBlocks * S * 4);
   DSA_DEBUG_CHECK((size_t)(p - (char*)ws) <= index_select_workspace_bytes(T, S));
   DSA_DEBUG_CHECK(filter_items(T, S) >= 1 && filter_items(T, S) <= INT32_MAX);
-  zero_i32_kernel<<<1, 64, 0, st>>>(fb, 1);
+  zero_heads_kernel<<<1, 64, 0, st>>>(fb, gq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   idx_estimate_kernel<<<(unsigned)((T + 15) / 16), kEstWaves * 64, 0, st>>>(qf, qs, k8, ks, T, S, topk, tau);
@@ -829,12 +1118,18 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
   // bitmap words of the longest row with a bitmap, or the bucket pass's words
   const int64_t bn = S < kSelBitmapN ? S : kSelBitmapN;
   const int64_t words = S > kSelBitmapN && 2 * kOutBuckets > (bn + 31) / 32 ? 2 * kOutBuckets : (bn + 31) / 32;
+  const size_t lds_fast = (size_t)((bn + 127) / 128) * 16;
   const size_t lds = (size_t)2 * kSelMax * 4 + (size_t)words * 4;
   static std::atomic<uint64_t> attr_done{0};
-  e = set_lds_limit_once((const void*)idx_select_kernel, (int)(2 * kSelMax * 4 + (kSelBitmapN / 32) * 4), attr_done);
+  e = set_lds_limit_once((const void*)idx_select_generic_kernel, (int)(2 * kSelMax * 4 + (kSelBitmapN / 32) * 4),
+                         attr_done);
   if (e != hipSuccess) return e;
-  idx_select_kernel<<<(unsigned)T, kSelThreads, lds, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, fb,
-                                                          force_fallback ? 1 : 0, dyn);
+  idx_select_fast_kernel<<<(unsigned)T, kSfThreads, lds_fast, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, gq, fb,
+                                                                   force_fallback ? 1 : 0, dyn);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned gen_blocks = (unsigned)(T < kGenericBlocks ? T : kGenericBlocks);
+  idx_select_generic_kernel<<<gen_blocks, kSelThreads, lds, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, gq, fb,
+                                                                 dyn);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   idx_fallback_kernel<<<kFbBlocks, kTopkThreads, 0, st>>>(qf, qs, k8, ks, S, S - T, topk, fb, scratch, idx_out,
                                                           dyn);
