@@ -397,7 +397,6 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
   __shared__ uint32_t tring[kFiltWaves][kRing];              // ... and its tag
   __shared__ uint32_t rcnt[kFiltWaves][64 * kSeg];           // per (row of the wave, segment)
   __shared__ float tvtab[kFiltWaves][64];                    // per row: survivor threshold on v
-  __shared__ int tqtab[kFiltWaves][64];                      // ... and the last key it sees
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
   const FilterItem item = filter_item(blockIdx.x, T, S);
@@ -473,58 +472,69 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
     tq[q] = ok ? (int)(S - T + t) : -1;  // key bound (position); an invalid query masks every key
     const float ta = tau[tt];
     // survivors need v * qs >= tau; shave a few ulps so rounding of the
-    // product can never drop a key whose final score reaches tau
-    tv[q] = !ok ? INFINITY : ta == -INFINITY ? -INFINITY : (ta / qs[tt]) * (1.0f - 1.0f / (1 << 20));
+    // product can never drop a key whose final score reaches tau.  A row
+    // that keeps every key gets -FLT_MAX: every finite score passes, a
+    // masked (-inf) one does not
+    tv[q] = !ok ? INFINITY : ta == -INFINITY ? -3.402823466e38f : (ta / qs[tt]) * (1.0f - 1.0f / (1 << 20));
   }
   if (g == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tvtab[w][16 * q + c] = tv[q];
-      tqtab[w][16 * q + c] = tq[q];
-    }
+    for (int q = 0; q < 4; ++q) tvtab[w][16 * q + c] = tv[q];
   }
-  // tag of a group: key offset of its first key from the item's first key
-  // << 6, then the row within the wave (16 q + c)
-  const uint32_t lane_tag = (uint32_t)((4 * g) << 6) | (uint32_t)c;
+  // tag of a group: bits 0-5 its row within the wave (16 q + c), bits 6-7
+  // its segment, bits 8-31 the key offset of its first key from the item's
+  // first key.  The segment depends only on the 16-key step, so a step's
+  // tags share one wave-uniform part.
+  const uint32_t lane_tag = (uint32_t)((4 * g) << 8) | (uint32_t)c;
   uint32_t ptr = 0, tail = 0;   // ring write and flush positions (wave-uniform)
 
-  // one flush round: up to 64 ring groups, one per lane
-  uint2* const wave_seg = cand + (Q0 * kSets + item.set) * kSeg * (int64_t)kSegStride;
+  // one flush round: up to 64 ring groups, one per lane.  Keys past a row's
+  // position never reach the ring (the epilogue masks them), so only the
+  // threshold is tested here; a segment's survivors past kCap all land in
+  // its slot kCap (never read: the count reports the overflow).
+  char* const wave_seg = (char*)(cand + (Q0 * kSets + item.set) * kSeg * (int64_t)kSegStride);
+  const uint32_t k0 = (uint32_t)item.k0;
   auto flush = [&](uint32_t n) {
     const v4f vv = vr[tail + lane];
     const uint32_t tag = tr[tail + lane];
-    const int rl = (int)(tag & 63u);
-    const uint32_t koff = tag >> 6;
-    const int sg = seg_of(koff);
+    const uint32_t rl = tag & 63u, sg = (tag >> 6) & 3u;
     const float tvr = tvtab[w][rl];
-    const int tqr = tqtab[w][rl];
-    const int key0 = (int)(item.k0 + koff);
     const bool live = (uint32_t)lane < n;
     bool p[4];
     uint32_t np = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = live & (vv[i] >= tvr) & (key0 + i <= tqr);
+      p[i] = live & (vv[i] >= tvr);
       np += p[i] ? 1u : 0u;
     }
     uint32_t r = 0;
     if (np) r = atomicAdd(&rc[sg * 64 + rl], np);
     // segment (row Q0 + rl, this item's key chunk, sg) within the wave's rows
-    uint2* const dst = wave_seg + (uint32_t)(rl * (kSets * kSeg) + sg) * (uint32_t)kSegStride;
+    const uint32_t seg = (rl * (kSets * kSeg) + sg) * (uint32_t)kSegStride;
+    const uint32_t key0 = k0 + (tag >> 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (p[i] && r < (uint32_t)kCap) dst[r] = make_uint2(__float_as_uint(vv[i]), (uint32_t)(key0 + i));
+      if (p[i]) {
+        const uint32_t off = (seg + min(r, (uint32_t)kCap)) * 8u;
+        *(uint2*)(wave_seg + off) = make_uint2(__float_as_uint(vv[i]), key0 + (uint32_t)i);
+      }
       r += p[i] ? 1u : 0u;
     }
     tail += n;
   };
 
-  // groups of one 16-key step (kt) of a tile: four MFMA results, one per
-  // query group q, four scores per lane
-  auto epilogue = [&](const v4f (&acc)[4], const v4f& kss, uint32_t step_tag) {
+  // groups of one 16-key step of a tile: four MFMA results, one per query
+  // group q, four scores per lane.  On tiles that reach past the wave's
+  // first row position (`masked`), scores of keys past a row's position
+  // become -inf; key_lane is the key of the lane's first score.
+  auto epilogue = [&](const v4f (&acc)[4], const v4f& kss, uint32_t step_tag, bool masked, int key_lane) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const v4f v = {acc[q][0] * kss[0], acc[q][1] * kss[1], acc[q][2] * kss[2], acc[q][3] * kss[3]};
+      v4f v = {acc[q][0] * kss[0], acc[q][1] * kss[1], acc[q][2] * kss[2], acc[q][3] * kss[3]};
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = key_lane + i <= tq[q] ? v[i] : -INFINITY;
+      }
       const bool pass = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) >= tv[q];
       const uint64_t m = ballot(pass);
       if (pass) {
@@ -571,23 +581,32 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
   // epilogue of step s; the barrier that hands over the next tile sits
   // between the last read of one tile and the first of the next (the
   // epilogue only reads registers and the wave's own ring)
+  // tiles [0, nsafe) end at or below the wave's first row position
+  const int64_t pq = S - T + Q0;
+  const int nsafe = pq >= item.k0 ? (int)min((int64_t)ntiles, (pq - item.k0 + 1) / kFiltKeys) : 0;
+  // wave-uniform tag part of step kt of tile it: key offset and segment
+  auto step_tag = [&](int it, int kt) {
+    const uint32_t koff = (uint32_t)(it * kFiltKeys + 16 * kt);
+    return (koff << 8) | ((uint32_t)seg_of(koff) << 6);
+  };
   lds_barrier();   // the producer's first tile
   v4f acc_a[4], acc_b[4], kss_a, kss_b;
   if (ntiles > 0) mfmas(0, 0, acc_a, kss_a);
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it % kFiltBufs;
-    const uint32_t tag0 = ((uint32_t)(it * kFiltKeys) << 6) + lane_tag;
+    const bool masked = it >= nsafe;
+    const int key_lane = (int)(item.k0 + it * kFiltKeys + 4 * g);
     mfmas(buf, 1, acc_b, kss_b);
-    epilogue(acc_a, kss_a, tag0);
+    epilogue(acc_a, kss_a, step_tag(it, 0) + lane_tag, masked, key_lane);
     mfmas(buf, 2, acc_a, kss_a);
-    epilogue(acc_b, kss_b, tag0 + (16u << 6));
+    epilogue(acc_b, kss_b, step_tag(it, 1) + lane_tag, masked, key_lane + 16);
     mfmas(buf, 3, acc_b, kss_b);
-    epilogue(acc_a, kss_a, tag0 + (32u << 6));
+    epilogue(acc_a, kss_a, step_tag(it, 2) + lane_tag, masked, key_lane + 32);
     if (it + 1 < ntiles) {
       lds_barrier();   // done with tile it; tile it + 1 has landed
       mfmas((it + 1) % kFiltBufs, 0, acc_a, kss_a);
     }
-    epilogue(acc_b, kss_b, tag0 + (48u << 6));
+    epilogue(acc_b, kss_b, step_tag(it, 3) + lane_tag, masked, key_lane + 48);
   }
   if (ptr != tail) flush(ptr - tail);
 
@@ -1084,7 +1103,8 @@ size_t index_select_workspace_bytes(int64_t T, int64_t S) {
   return b;
 }
 
-bool index_select_supported(int64_t T, int64_t S) { return T >= 1 && S >= T && S <= (int64_t(1) << 31) - 1; }
+// survivor tags hold key offsets below kmax in 24 bits
+bool index_select_supported(int64_t T, int64_t S) { return T >= 1 && S >= T && S <= (int64_t(1) << 25); }
 
 hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t* k8, const float* ks,
                                int64_t T, int64_t S, int64_t topk, int32_t* idx_out, void* ws,
