@@ -394,7 +394,7 @@ constexpr int kMlaTile = 32 * (576 / 8) * 16;         // 32 latent rows, 36 KB
 constexpr size_t kMlaFixedLds = 3 * kMlaTile + 2 * 8 * 1024;
 
 #ifndef DSA_MLA_QKG
-#define DSA_MLA_QKG 3  // k-steps of S^T read per LDS round trip (2 fragments each)
+#define DSA_MLA_QKG 2  // k-steps of S^T read per LDS round trip (2 fragments each)
 #endif
 
 // 2^x with the hardware instruction alone: results below 2^-126 flush to
@@ -487,22 +487,28 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
     const int j0 = kbeg + jl * NK;
     __builtin_amdgcn_s_setprio(1);
     v4f sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
+    // K fragments in a rolling pipeline: the reads of k-step kk + D are
+    // issued before the MFMAs of k-step kk, so D steps of reads are in
+    // flight behind the matrix core (the same registers as D reads per
+    // round trip)
+    constexpr int D = DSA_MLA_QKG;
+    v8s k0[KK], k1[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; kk += DSA_MLA_QKG) {
-      v8s k0[DSA_MLA_QKG], k1[DSA_MLA_QKG];
+    for (int kk = 0; kk < D; ++kk) {
+      k0[kk] = *(const v8s*)(tb + (kk * 64 + lane) * 16);
+      k1[kk] = *(const v8s*)(tb + ((VF + kk) * 64 + lane) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < DSA_MLA_QKG; ++u) {
-        k0[u] = *(const v8s*)(tb + ((kk + u) * 64 + lane) * 16);
-        k1[u] = *(const v8s*)(tb + ((VF + kk + u) * 64 + lane) * 16);
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + D < KK) {
+        k0[kk + D] = *(const v8s*)(tb + ((kk + D) * 64 + lane) * 16);
+        k1[kk + D] = *(const v8s*)(tb + ((VF + kk + D) * 64 + lane) * 16);
       }
-#pragma unroll
-      for (int u = 0; u < DSA_MLA_QKG; ++u) {
-        sc0 = mfma_bf16_16x16x32(k0[u], qf[kk + u], sc0);
-        sc1 = mfma_bf16_16x16x32(k1[u], qf[kk + u], sc1);
-      }
-      // all of the group's reads in flight before its first MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DSA_MLA_QKG, 0);  // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * DSA_MLA_QKG, 0);  // MFMAs
+      sc0 = mfma_bf16_16x16x32(k0[kk], qf[kk], sc0);
+      sc1 = mfma_bf16_16x16x32(k1[kk], qf[kk], sc1);
+      if (kk + D < KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads of k-step kk + D
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                  // MFMAs of k-step kk
       __builtin_amdgcn_sched_barrier(0);
     }
     // keys past the block's last valid entry (last tile only) drop out
