@@ -6,9 +6,11 @@
 // amax/448 scale so that the pair product stays FP8.
 //
 // Work: T x 128 x 128 MACs in fp64 (bit-reproducible codes), ~1/1024 of the
-// indexer's pair work.  One thread owns one output column j and keeps column
-// j of W in registers; a block walks kRows query rows held in LDS as fp64.
-// Short batches split each column's sum over four waves instead.
+// indexer's pair work.  Long prefills with a bf16 W run a register-tiled
+// kernel (64 rows per block, 8 x 4 fp64 accumulators per thread); the fp32-W
+// configuration has one thread own one output column j with column j of W in
+// registers while a block walks its query rows held in LDS as fp64; short
+// batches split each column's sum over four waves instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -155,6 +157,110 @@ __global__ __launch_bounds__(512) void fold_split_kernel(const void* __restrict_
   }
 }
 
+// Long prefills (FP8 input, bf16 W): tiles of 64 rows, 256 threads, each
+// thread a register tile of 8 rows x 4 columns (32 fp64 accumulators), the
+// rows' dequantised values as fp64 in LDS (k-major, so a thread's 8 rows are
+// one 64-byte read) and W as fp32 in LDS (4 columns in one 16-byte read):
+// per k, 5 LDS reads and 4 conversions feed 32 fp64 FMAs.  A block converts
+// W once and walks tiles blockIdx.x, blockIdx.x + gridDim.x, ..., loading
+// the next tile's codes (32 bytes per thread) while it computes the current
+// one.  The per-row amax is a reduction over the 32 threads sharing the row.
+constexpr int kTileRows = 64;
+__global__ __launch_bounds__(256, 1) void fold_tile_kernel(const uint8_t* __restrict__ q_in,
+                                                           const float* __restrict__ q_scale,
+                                                           const uint16_t* __restrict__ w_in, int64_t T,
+                                                           uint8_t* __restrict__ q_out, float* __restrict__ s_out) {
+  extern __shared__ __align__(16) char fold_smem[];
+  float* sw = (float*)fold_smem;                                    // [k][j], 64 KB
+  double* sq = (double*)(fold_smem + kIdxDim * kIdxDim * 4);        // [k][row], 64 KB
+  const int tid = threadIdx.x;
+  const int tx = tid & 31, ty = tid >> 5;   // columns 4 tx .. +3, rows 8 ty .. +7
+  const int lr = tid >> 2, lk = 32 * (tid & 3);  // the codes this thread loads: row lr, dims lk .. lk+31
+  const int64_t ntile = (T + kTileRows - 1) / kTileRows;
+  {
+    uint4 wb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wb[i] = ((const uint4*)w_in)[tid + 256 * i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 8 * (tid + 256 * i);
+      const uint32_t u[4] = {wb[i].x, wb[i].y, wb[i].z, wb[i].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        *(float2*)(sw + e + 2 * h) = make_float2(__uint_as_float(u[h] << 16), __uint_as_float(u[h] & 0xFFFF0000u));
+    }
+  }
+  auto load = [&](int64_t tile, v8i& codes, float& scale) {
+    const int64_t t = tile * kTileRows + lr;
+    if (tile < ntile && t < T) {
+      codes = *(const v8i*)(q_in + t * kIdxDim + lk);
+      scale = q_scale[t];
+    } else {
+      codes = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+      scale = 0.f;
+    }
+  };
+  v8i codes;
+  float scale;
+  load(blockIdx.x, codes, scale);
+  for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
+    __syncthreads();   // the previous tile's reads of sq are done
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t c = ((uint32_t)codes[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      sq[(lk + j) * kTileRows + lr] = (double)e4m3_to_f32(c) * (double)scale;
+    }
+    __syncthreads();
+    load(tile + gridDim.x, codes, scale);
+    double acc[8][4];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+    // the LDS reads of step k + 1 are issued before the FMAs of step k
+    auto rd = [&](int k, float4& wv, double2 (&qv)[4]) {
+      wv = *(const float4*)(sw + k * kIdxDim + 4 * tx);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qv[r] = *(const double2*)(sq + k * kTileRows + 8 * ty + 2 * r);
+    };
+    auto fmas = [&](const float4& wv, const double2 (&qv)[4]) {
+      const double w4[4] = {(double)wv.x, (double)wv.y, (double)wv.z, (double)wv.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[2 * r][c] = fma(qv[r].x, w4[c], acc[2 * r][c]);
+          acc[2 * r + 1][c] = fma(qv[r].y, w4[c], acc[2 * r + 1][c]);
+        }
+    };
+    float4 wa, wb;
+    double2 qa[4], qb[4];
+    rd(0, wa, qa);
+    for (int k = 0; k < kIdxDim; k += 2) {
+      rd(k + 1, wb, qb);
+      fmas(wa, qa);
+      if (k + 2 < kIdxDim) rd(k + 2, wa, qa);
+      fmas(wb, qb);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t t = tile * kTileRows + 8 * ty + r;
+      double m = fmax(fmax(fabs(acc[r][0]), fabs(acc[r][1])), fmax(fabs(acc[r][2]), fabs(acc[r][3])));
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+      const float sc = m > 0.0 ? (float)(m / 448.0) : 1.0f;
+      if (t < T) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pk |= f64_to_e4m3_rne_sat(acc[r][c] / (double)sc) << (8 * c);
+        *(uint32_t*)(q_out + t * kIdxDim + 4 * tx) = pk;
+        if (tx == 0) s_out[t] = sc;
+      }
+    }
+  }
+}
+constexpr size_t kFoldTileLds = (size_t)kIdxDim * kIdxDim * 4 + (size_t)kIdxDim * kTileRows * 8;
+
 template <int R>
 static void launch_fold_rows(const void* q_in, const float* q_scale, bool fp8_in, const void* w, bool w_bf16,
                              int64_t T, void* q_out, float* s_out, hipStream_t st) {
@@ -170,7 +276,24 @@ static void launch_fold_rows(const void* q_in, const float* q_scale, bool fp8_in
 hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, const void* w,
                        bool w_bf16, int64_t T, void* q_out, float* s_out, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (T >= 8192)
+  // the tiled kernel's vector accesses: 32-byte code rows, 16-byte W reads,
+  // 4-byte packed stores
+  const bool tile_ok = ((uintptr_t)q_in % 32 == 0) && ((uintptr_t)w % 16 == 0) && ((uintptr_t)q_out % 4 == 0);
+  if (T >= 8192 && fp8_in && w_bf16 && tile_ok) {
+    static std::atomic<uint64_t> lds_done{0};
+    const hipError_t e = set_lds_limit_once((const void*)fold_tile_kernel, (int)kFoldTileLds, lds_done);
+    if (e != hipSuccess) return e;
+    int cus = 256;
+    {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    }
+    const int64_t tiles = (T + kTileRows - 1) / kTileRows;
+    fold_tile_kernel<<<(unsigned)(tiles < cus ? tiles : cus), 256, kFoldTileLds, st>>>(
+        (const uint8_t*)q_in, q_scale, (const uint16_t*)w, T, (uint8_t*)q_out, s_out);
+  } else if (T >= 8192)
     launch_fold_rows<32>(q_in, q_scale, fp8_in, w, w_bf16, T, q_out, s_out, st);
   else {
     dim3 grid((unsigned)((T + 1) / 2));

@@ -13,10 +13,9 @@
 //     keys in the A operand and queries in the B operand, so a lane owns one
 //     query and four keys; a score v = acc * ks survives if v >= tau_t / qs_t
 //     (rounded down a little, so the survivors contain every key whose final
-//     score u = v * qs reaches tau).  Survivors (v, key) are appended to one
-//     of four per-row segments, the segment picked by the lane group; a
-//     per-tile rotation of the key order spreads periodic key patterns over
-//     the segments.
+//     score u = v * qs reaches tau).  Survivors (v, key) are appended to
+//     the row's segment for that key chunk (one segment per row and chunk
+//     keeps few partly written cache lines open at a time).
 //  3. select: per row, u = v * qs and ReLU for each survivor, an exact radix
 //     select of the m best (score desc, index asc), and ascending output via
 //     a bitmap over key positions (position buckets for rows past 256K).  The survivors provably contain the exact
@@ -31,10 +30,13 @@
 #include "kernels.h"
 #include "select.h"
 
+#include <climits>
+#include <type_traits>
+
 namespace dsa {
 
-constexpr int kSeg = 4;                    // survivor segments per row
-constexpr int kCap = 1536;                 // survivors per segment
+constexpr int kSeg = 1;                    // survivor segments per row and key chunk
+constexpr int kCap = 6144;                 // survivors per segment
 constexpr int kTakeAll = 5632;             // rows this short keep every key
 constexpr int kSampleMax = 4096;           // samples per row (max)
 constexpr float kAlpha = 1.75f;            // survivor target / m
@@ -373,10 +375,13 @@ inline int64_t filter_items(int64_t T, int64_t S) {
 //     group: it keeps the scores that pass exactly (threshold and causal
 //     position), takes their places in the row's segment with one LDS
 //     atomic, and stores them; a round's stores are 64 lanes wide.
-// The four 16-key groups of every aligned 64-key block go to the row's four
-// segments in an order rotated by a hash of the block: a row that keeps
-// every key fills its segments evenly, and periodic key patterns (one
-// planted key per 64) spread over all four.
+// With kSeg > 1 the 16-key groups of every aligned 64-key block would go to
+// the row's segments in an order rotated by a hash of the block.  One
+// segment per row is the faster choice: the survivor stores of a block then
+// keep 256 partly written cache lines open instead of 1024, so fewer lines
+// leave the XCD's L2 before they fill (at 131072 tokens, 3.8 GB of
+// survivors were written back as 10.6 GB with four segments, 8.6 GB with
+// one).
 constexpr int kFiltWaves = kFiltRows / 64;
 constexpr int kFiltThreads = (kFiltWaves + 1) * 64;
 constexpr int kFiltBufs = 3;
@@ -384,10 +389,10 @@ constexpr int kRing = 256;      // group slots per compute wave's ring
 constexpr int kTileCopies = 9;  // copies per key tile: 8 of key bytes, 1 of scales
 
 __device__ __forceinline__ int seg_of(uint32_t koff) {
-  return (int)(((koff >> 4) + (((koff >> 6) * 0x9E3779B1u) >> 30)) & 3u);
+  return (int)(((koff >> 4) + (((koff >> 6) * 0x9E3779B1u) >> 30)) & (uint32_t)(kSeg - 1));
 }
 
-__global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
+__global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k8,
     const float* __restrict__ ks, int64_t T, int64_t S, const float* __restrict__ tau,
     uint2* __restrict__ cand, int32_t* __restrict__ cnt_out) {
@@ -463,6 +468,7 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
   v8i bq[4];
   int tq[4];
   float tv[4];
+  int tvb[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t t = Q0 + 16 * q + c;
@@ -476,6 +482,11 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
     // that keeps every key gets -FLT_MAX: every finite score passes, a
     // masked (-inf) one does not
     tv[q] = !ok ? INFINITY : ta == -INFINITY ? -3.402823466e38f : (ta / qs[tt]) * (1.0f - 1.0f / (1 << 20));
+    // the same test on the bit patterns as signed integers, exact for a
+    // threshold >= +0 (negative scores and -inf order below every
+    // non-negative float); a row that keeps every key lets every group in
+    // and the flush's float compare drops its masked scores
+    tvb[q] = tv[q] < 0.f ? INT_MIN : __float_as_int(tv[q]);
   }
   if (g == 0) {
 #pragma unroll
@@ -489,9 +500,10 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
   uint32_t ptr = 0, tail = 0;   // ring write and flush positions (wave-uniform)
 
   // one flush round: up to 64 ring groups, one per lane.  Keys past a row's
-  // position never reach the ring (the epilogue masks them), so only the
-  // threshold is tested here; a segment's survivors past kCap all land in
-  // its slot kCap (never read: the count reports the overflow).
+  // position never pass the float compare (the epilogue masks them to
+  // -inf), so only the threshold is tested here; a segment's survivors past
+  // kCap all land in its slot kCap (never read: the count reports the
+  // overflow).
   char* const wave_seg = (char*)(cand + (Q0 * kSets + item.set) * kSeg * (int64_t)kSegStride);
   const uint32_t k0 = (uint32_t)item.k0;
   auto flush = [&](uint32_t n) {
@@ -524,44 +536,62 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
   };
 
   // groups of one 16-key step of a tile: four MFMA results, one per query
-  // group q, four scores per lane.  On tiles that reach past the wave's
-  // first row position (`masked`), scores of keys past a row's position
-  // become -inf; key_lane is the key of the lane's first score.
-  auto epilogue = [&](const v4f (&acc)[4], const v4f& kss, uint32_t step_tag, bool masked, int key_lane) {
+  // group q, four scores per lane, taken in two halves of two q each: both
+  // pass tests first, then one wave-uniform branch appends the passing
+  // groups to the ring and flushes whole rounds.  On tiles that reach past
+  // the wave's first row position (MASKED), scores of keys past a row's
+  // position become -inf; key_lane is the key of the lane's first score.
+  auto epilogue = [&](bool MASKED, const v4f (&acc)[4], const v4f& kss, uint32_t step_tag, int key_lane) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v4f v = {acc[q][0] * kss[0], acc[q][1] * kss[1], acc[q][2] * kss[2], acc[q][3] * kss[3]};
-      if (masked) {
+    for (int q0 = 0; q0 < 4; q0 += 2) {
+      v4f v[2];
+      bool pass[2];
+      uint64_t mk[2];
+      uint32_t tot = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = key_lane + i <= tq[q] ? v[i] : -INFINITY;
-      }
-      const bool pass = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])) >= tv[q];
-      const uint64_t m = ballot(pass);
-      if (pass) {
-        // wave-uniform bases, the lane's rank among the passing lanes
-        v4f* const vb = vr + ptr;
-        uint32_t* const tb = tr + ptr;
-        const uint32_t rank = lanes_below(m);
-        vb[rank] = v;
-        tb[rank] = step_tag + (uint32_t)(16 * q);
-      }
-      ptr += (uint32_t)__popcll(m);
-      // at most 64 new groups per step: one round brings the ring below 64;
-      // when the next step might run past its end, the (< 64) live groups
-      // move to its front
-      if (ptr - tail >= 64u) flush(64u);
-      if (ptr > (uint32_t)(kRing - 64)) {
-        const uint32_t nl = ptr - tail;
-        const v4f e = vr[tail + lane];
-        const uint32_t et = tr[tail + lane];
-        __builtin_amdgcn_wave_barrier();
-        if ((uint32_t)lane < nl) {
-          vr[lane] = e;
-          tr[lane] = et;
+      for (int j = 0; j < 2; ++j) {
+        const int q = q0 + j;
+        v[j] = (v4f){acc[q][0] * kss[0], acc[q][1] * kss[1], acc[q][2] * kss[2], acc[q][3] * kss[3]};
+        if (MASKED) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[j][i] = key_lane + i <= tq[q] ? v[j][i] : -INFINITY;
         }
-        __builtin_amdgcn_wave_barrier();
-        tail = 0;
-        ptr = nl;
+        const int mx = max(max(__float_as_int(v[j][0]), __float_as_int(v[j][1])),
+                           max(__float_as_int(v[j][2]), __float_as_int(v[j][3])));
+        pass[j] = mx >= tvb[q];
+        mk[j] = ballot(pass[j]);
+        tot += (uint32_t)__popcll(mk[j]);
+      }
+      // before each half at most 63 groups are live and the ring has room
+      // for the half's at most 128 new ones
+      if (tot) {
+        uint32_t base = ptr;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (pass[j]) {
+            const uint32_t rank = base + lanes_below(mk[j]);
+            vr[rank] = v[j];
+            tr[rank] = step_tag + (uint32_t)(16 * (q0 + j));
+          }
+          base += (uint32_t)__popcll(mk[j]);
+        }
+        ptr = base;
+        while (ptr - tail >= 64u) flush(64u);
+        // when the next half might run past the ring's end, the (< 64) live
+        // groups move to its front
+        if (ptr > (uint32_t)(kRing - 128)) {
+          const uint32_t nl = ptr - tail;
+          const v4f e = vr[tail + lane];
+          const uint32_t et = tr[tail + lane];
+          __builtin_amdgcn_wave_barrier();
+          if ((uint32_t)lane < nl) {
+            vr[lane] = e;
+            tr[lane] = et;
+          }
+          __builtin_amdgcn_wave_barrier();
+          tail = 0;
+          ptr = nl;
+        }
       }
     }
   };
@@ -592,21 +622,23 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
   lds_barrier();   // the producer's first tile
   v4f acc_a[4], acc_b[4], kss_a, kss_b;
   if (ntiles > 0) mfmas(0, 0, acc_a, kss_a);
-  for (int it = 0; it < ntiles; ++it) {
+  auto tile = [&](bool masked_c, int it) {
     const int buf = it % kFiltBufs;
-    const bool masked = it >= nsafe;
     const int key_lane = (int)(item.k0 + it * kFiltKeys + 4 * g);
     mfmas(buf, 1, acc_b, kss_b);
-    epilogue(acc_a, kss_a, step_tag(it, 0) + lane_tag, masked, key_lane);
+    epilogue(masked_c, acc_a, kss_a, step_tag(it, 0) + lane_tag, key_lane);
     mfmas(buf, 2, acc_a, kss_a);
-    epilogue(acc_b, kss_b, step_tag(it, 1) + lane_tag, masked, key_lane + 16);
+    epilogue(masked_c, acc_b, kss_b, step_tag(it, 1) + lane_tag, key_lane + 16);
     mfmas(buf, 3, acc_b, kss_b);
-    epilogue(acc_a, kss_a, step_tag(it, 2) + lane_tag, masked, key_lane + 32);
+    epilogue(masked_c, acc_a, kss_a, step_tag(it, 2) + lane_tag, key_lane + 32);
     if (it + 1 < ntiles) {
       lds_barrier();   // done with tile it; tile it + 1 has landed
       mfmas((it + 1) % kFiltBufs, 0, acc_a, kss_a);
     }
-    epilogue(acc_b, kss_b, step_tag(it, 3) + lane_tag, masked, key_lane + 48);
+    epilogue(masked_c, acc_b, kss_b, step_tag(it, 3) + lane_tag, key_lane + 48);
+  };
+  for (int it = 0; it < ntiles; ++it) {
+    tile(it >= nsafe, it);
   }
   if (ptr != tail) flush(ptr - tail);
 
@@ -617,6 +649,7 @@ __global__ __launch_bounds__(kFiltThreads, 2) void idx_filter_kernel(
     const int rl = 16 * q + c;
     const int64_t t = Q0 + rl;
     // lane group g reports segment g of its rows
+    if (g >= kSeg) continue;
     const uint32_t n = rc[g * 64 + rl];
     cnt_out[(t * kSets + item.set) * kSeg + g] = n > (uint32_t)kCap ? kCap + 1 : (int)n;
     if (!two) cnt_out[(t * kSets + 1) * kSeg + g] = 0;  // rows with one key chunk
