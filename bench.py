@@ -145,7 +145,8 @@ def probe_peaks(torch, dev):
         return best
 
     out = {"method": "probe library: MFMA issue loops (8 independent accumulators per wave, 2 workgroups of "
-                     "4 waves per CU) and a 16-byte-load streaming read of 4 GiB; best of 3 launches"}
+                     "4 waves per CU) and a streaming read of 4 GiB (2 workgroups per CU, each a contiguous "
+                     "slice, 16-byte non-temporal loads, 8 in flight per thread); best of 3 launches"}
     iters = 4096
     for kind, key in ((0, "fp8_tflops"), (1, "bf16_16x16x32_tflops"), (2, "bf16_32x32x16_tflops")):
         lib.dsa_probe_mfma(kind, 16, blocks, ctypes.c_void_p(sink.data_ptr()), sp)   # warm-up
@@ -154,7 +155,7 @@ def probe_peaks(torch, dev):
     out["bf16_tflops"] = max(out["bf16_16x16x32_tflops"], out["bf16_32x32x16_tflops"])
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
-    rblocks = 8 * cus
+    rblocks = 2 * cus
     rsink = torch.empty(rblocks * 256, dtype=torch.float32, device=dev)
     lib.dsa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks, ctypes.c_void_p(rsink.data_ptr()), sp)
     ms = timed(lambda: lib.dsa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks,

@@ -15,10 +15,11 @@
  *     2  v_mfma_f32_32x32x16_bf16  (32768 FLOP each)
  *   and writes one float per thread to sink[blocks * 256] (so the work is
  *   kept).  dsa_probe_mfma_flops() returns the FLOPs one such launch does.
- * dsa_probe_read: streams `bytes` (a multiple of 16 and of 16 * 256 *
- *   blocks) from `buf` with 16-byte loads, each thread walking its own
- *   blocks * 256-strided sequence, and writes one float per thread to
- *   sink[blocks * 256].
+ * dsa_probe_read: streams `bytes` (a multiple of 16 * 256 * 8 * blocks)
+ *   from `buf` (16-byte aligned): workgroup b of `blocks` reads the b-th
+ *   contiguous 1/blocks of the buffer with 16-byte non-temporal loads, eight
+ *   in flight per thread, and writes one float per thread to
+ *   sink[blocks * 256].  Returns -1 for sizes that do not divide.
  */
 #ifndef DSA_PROBE_H_
 #define DSA_PROBE_H_

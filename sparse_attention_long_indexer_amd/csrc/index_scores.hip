@@ -121,41 +121,75 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
 // ---- decode: one query per sequence against its own cache ----------------
 //
 // Bound by the HBM read of the cached index keys (132 bytes per key with its
-// scale).  Block (x, b) covers 512 keys of sequence b, 128 per wave; the
-// query row is replicated over the 16 A rows so every C row holds the same
-// 16 scores.  Every key and scale load of a wave is issued before the first
-// MFMA (clamped addresses, no branches), so each wave keeps 16 KB in flight.
-constexpr int kDecWaveKeys = 128;
+// scale).  Block (x, b) covers 256 keys of sequence b, 64 per wave.  A wave
+// copies its 64 keys (8 KB, contiguous in the cache) straight into its own
+// LDS region with eight 1 KB direct-to-LDS copies, each covering 8 whole key
+// rows (8 lanes per 128-byte row), issued non-temporal since every cached
+// key is read once per step; then reads them back in the MFMA's operand
+// layout.  Within a row the 16-byte chunk j of key r sits in slot
+// j ^ ((r >> 1) & 7), so that the 16 lanes reading one chunk of 16
+// consecutive keys hit 16 distinct bank groups.  The query row is
+// replicated over the 16 A rows so every C row holds the same 16 scores.
+#ifndef DSA_DEC_WAVE_KEYS
+#define DSA_DEC_WAVE_KEYS 64
+#endif
+#ifndef DSA_DEC_NT
+#define DSA_DEC_NT 2
+#endif
+constexpr int kDecWaveKeys = DSA_DEC_WAVE_KEYS;
 constexpr int kDecKeysPerBlock = 4 * kDecWaveKeys;
+constexpr int kNtAux = DSA_DEC_NT;   // cache-policy operand of the copies: 2 = non-temporal
 
 __global__ __launch_bounds__(256) void index_scores_decode_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const int64_t* __restrict__ off, int64_t b0, float* __restrict__ out) {
-  constexpr int J = kDecWaveKeys / 16;
+  constexpr int J = kDecWaveKeys / 16;   // 16-key MFMA groups per wave
+  constexpr int NI = kDecWaveKeys / 8;   // 1 KB copies per wave
+  __shared__ __align__(16) uint8_t kbuf[4][kDecWaveKeys * kIdxDim];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int64_t b = b0 + blockIdx.y;
   const int64_t lo = off[b], n = off[b + 1] - lo;
   const int64_t sw = (int64_t)blockIdx.x * kDecKeysPerBlock + w * kDecWaveKeys;
   if (sw >= n) return;
-  v8i bb[J];
+  // copy i: lane l brings chunk (l % 8) ^ f(r) of key r = 8 i + l / 8 (keys
+  // past the sequence's end read its last key; their scores are dropped)
+  {
+    const int rl = lane >> 3;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = 8 * i + rl;
+      const int64_t s = sw + r;
+      const int64_t sb = lo + (s < n ? s : n - 1);
+      const int j = (lane & 7) ^ ((r >> 1) & 7);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(k + sb * kIdxDim + 16 * j),
+          (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint8_t*)kbuf[w] + 1024 * i),
+          16, 0, kNtAux);
+    }
+  }
   float kss[J];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int64_t s = sw + 16 * j + c;
-    const int64_t sb = lo + (s < n ? s : n - 1);
-    bb[j] = *(const v8i*)(k + sb * kIdxDim + 32 * g);
-    kss[j] = ks[sb];
+  for (int jj = 0; jj < J; ++jj) {
+    const int64_t s = sw + 16 * jj + c;
+    kss[jj] = __builtin_nontemporal_load(ks + lo + (s < n ? s : n - 1));
   }
   const v8i a = *(const v8i*)(qf + b * kIdxDim + 32 * g);
   const float qsc = qs[b];
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed (its own LDS region)
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int64_t s = sw + 16 * j + c;
+  for (int jj = 0; jj < J; ++jj) {
+    const int r = 16 * jj + c;
+    const uint8_t* row = kbuf[w] + 1024 * (r >> 3) + 128 * (r & 7);
+    const int f = (r >> 1) & 7;
+    const v4i h0 = *(const v4i*)(row + 16 * ((2 * g) ^ f));
+    const v4i h1 = *(const v4i*)(row + 16 * ((2 * g + 1) ^ f));
+    const v8i bb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    const int64_t s = sw + r;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma_fp8_16x16x128(a, bb[j], acc);
+    acc = mfma_fp8_16x16x128(a, bb, acc);
     if (g == 0 && s < n) {
-      const float u = acc[0] * kss[j] * qsc;
+      const float u = acc[0] * kss[jj] * qsc;
       out[lo + s] = u > 0.f ? u : 0.f;
     }
   }

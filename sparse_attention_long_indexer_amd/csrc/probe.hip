@@ -70,22 +70,23 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int64_t iters, float* _
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = r;
 }
 
-__global__ __launch_bounds__(256) void probe_read_kernel(const uint4* __restrict__ buf, int64_t n16,
+// Streaming read: block b reads its own contiguous 1/gridDim of the buffer,
+// eight 16-byte non-temporal loads in flight per thread (the fastest of the
+// read patterns measured: 7.0-7.2 TB/s, against 6.2 TB/s with ordinary loads
+// and 5.3-5.6 TB/s for a grid-strided loop).
+__global__ __launch_bounds__(256) void probe_read_kernel(const v4i* __restrict__ buf, int64_t per_block,
                                                          float* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  uint32_t x = 0;
-  int64_t i = i0;
-  // four 16-byte loads in flight per thread
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  constexpr int U = 8;
+  const v4i* p = buf + (int64_t)blockIdx.x * per_block + threadIdx.x;
+  int x = 0;
+  for (int64_t i = 0; i < per_block; i += 256 * U) {
+    v4i v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + 256 * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n16; i += stride) {
-    const uint4 a = buf[i];
-    x ^= a.x ^ a.y ^ a.z ^ a.w;
-  }
-  sink[i0] = (float)(x & 0xFFFF);
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = (float)(x & 0xFFFF);
 }
 
 }  // namespace dsa
@@ -113,8 +114,8 @@ int dsa_probe_mfma(int kind, int64_t iters, int64_t blocks, float* sink, void* s
 
 int dsa_probe_read(const void* buf, int64_t bytes, int64_t blocks, float* sink, void* stream) {
   if (!buf || !sink || bytes <= 0 || blocks < 1 || blocks > 2147483647 || bytes % 16) return -1;
-  if ((bytes / 16) % (blocks * 256)) return -1;
-  probe_read_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>((const uint4*)buf, bytes / 16, sink);
+  if ((bytes / 16) % (blocks * 256 * 8)) return -1;
+  probe_read_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>((const v4i*)buf, bytes / 16 / blocks, sink);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
