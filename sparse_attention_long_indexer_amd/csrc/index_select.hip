@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
   // first key.  The segment depends only on the 16-key step, so a step's
   // tags share one wave-uniform part.
   const uint32_t lane_tag = (uint32_t)((4 * g) << 8) | (uint32_t)c;
-  uint32_t ptr = 0, tail = 0;   // ring write and flush positions (wave-uniform)
+  uint32_t ptr = 0, tail = 0;   // ring write and flush counts (wave-uniform; slots modulo kRing)
 
   // one flush round: up to 64 ring groups, one per lane.  Keys past a row's
   // position never pass the float compare (the epilogue masks them to
@@ -507,8 +507,8 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
   char* const wave_seg = (char*)(cand + (Q0 * kSets + item.set) * kSeg * (int64_t)kSegStride);
   const uint32_t k0 = (uint32_t)item.k0;
   auto flush = [&](uint32_t n) {
-    const v4f vv = vr[tail + lane];
-    const uint32_t tag = tr[tail + lane];
+    const v4f vv = vr[(tail + lane) & (kRing - 1)];
+    const uint32_t tag = tr[(tail + lane) & (kRing - 1)];
     const uint32_t rl = tag & 63u, sg = (tag >> 6) & 3u;
     const float tvr = tvtab[w][rl];
     const bool live = (uint32_t)lane < n;
@@ -562,14 +562,14 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
         mk[j] = ballot(pass[j]);
         tot += (uint32_t)__popcll(mk[j]);
       }
-      // before each half at most 63 groups are live and the ring has room
-      // for the half's at most 128 new ones
+      // the ring is circular (positions modulo kRing): before each half at
+      // most 63 groups are live, so the half's at most 128 new ones fit
       if (tot) {
         uint32_t base = ptr;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (pass[j]) {
-            const uint32_t rank = base + lanes_below(mk[j]);
+            const uint32_t rank = (base + lanes_below(mk[j])) & (uint32_t)(kRing - 1);
             vr[rank] = v[j];
             tr[rank] = step_tag + (uint32_t)(16 * (q0 + j));
           }
@@ -577,40 +577,29 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
         }
         ptr = base;
         while (ptr - tail >= 64u) flush(64u);
-        // when the next half might run past the ring's end, the (< 64) live
-        // groups move to its front
-        if (ptr > (uint32_t)(kRing - 128)) {
-          const uint32_t nl = ptr - tail;
-          const v4f e = vr[tail + lane];
-          const uint32_t et = tr[tail + lane];
-          __builtin_amdgcn_wave_barrier();
-          if ((uint32_t)lane < nl) {
-            vr[lane] = e;
-            tr[lane] = et;
-          }
-          __builtin_amdgcn_wave_barrier();
-          tail = 0;
-          ptr = nl;
-        }
       }
     }
   };
-  // one step's MFMAs: A row c (key kb + 16 kt + c), bytes 32 g .. 32 g + 31,
-  // in two lane-linear reads; the key scales of C rows 4g .. 4g+3
-  auto mfmas = [&](int buf, int kt, v4f (&acc)[4], v4f& kss) {
+  // one step's operands: A row c (key kb + 16 kt + c), bytes 32 g .. 32 g +
+  // 31, in two lane-linear reads; the key scales of C rows 4g .. 4g+3
+  auto rd = [&](int buf, int kt, v8i& a, v4f& kss) {
     const v4i a0 = *(const v4i*)(ktile[buf] + (2 * kt) * 1024 + 16 * lane);
     const v4i a1 = *(const v4i*)(ktile[buf] + (2 * kt + 1) * 1024 + 16 * lane);
-    const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    a = (v8i){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     kss = *(const v4f*)(&kst[buf][16 * kt + 4 * g]);
+  };
+  auto mfmas = [&](const v8i& a, v4f (&acc)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = mfma_fp8_16x16x128(a, bq[q], (v4f){0.f, 0.f, 0.f, 0.f});
   };
 
   // software pipeline over the four 16-key steps of each tile, two sets of
-  // accumulators in turn: the MFMAs of step s + 1 are issued before the
-  // epilogue of step s; the barrier that hands over the next tile sits
-  // between the last read of one tile and the first of the next (the
-  // epilogue only reads registers and the wave's own ring)
+  // accumulators in turn: the MFMAs of step s + 1 and the operand reads of
+  // step s + 2 are issued before the epilogue of step s (reads issued ahead
+  // of the epilogue's ring writes do not wait behind them); the barrier
+  // that hands over the next tile sits between the last read of one tile
+  // and the first of the next (the epilogue only reads registers and the
+  // wave's own ring)
   // tiles [0, nsafe) end at or below the wave's first row position
   const int64_t pq = S - T + Q0;
   const int nsafe = pq >= item.k0 ? (int)min((int64_t)ntiles, (pq - item.k0 + 1) / kFiltKeys) : 0;
@@ -620,20 +609,35 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
     return (koff << 8) | ((uint32_t)seg_of(koff) << 6);
   };
   lds_barrier();   // the producer's first tile
-  v4f acc_a[4], acc_b[4], kss_a, kss_b;
-  if (ntiles > 0) mfmas(0, 0, acc_a, kss_a);
+  v4f acc_a[4], acc_b[4], kss_a, kss_b, kss_n;
+  v8i an;
+  if (ntiles > 0) {
+    rd(0, 0, an, kss_a);
+    mfmas(an, acc_a);
+    rd(0, 1, an, kss_n);
+  }
   auto tile = [&](bool masked_c, int it) {
-    const int buf = it % kFiltBufs;
     const int key_lane = (int)(item.k0 + it * kFiltKeys + 4 * g);
-    mfmas(buf, 1, acc_b, kss_b);
+    const bool more = it + 1 < ntiles;
+    kss_b = kss_n;
+    mfmas(an, acc_b);
+    rd(it % kFiltBufs, 2, an, kss_n);
     epilogue(masked_c, acc_a, kss_a, step_tag(it, 0) + lane_tag, key_lane);
-    mfmas(buf, 2, acc_a, kss_a);
+    kss_a = kss_n;
+    mfmas(an, acc_a);
+    rd(it % kFiltBufs, 3, an, kss_n);
     epilogue(masked_c, acc_b, kss_b, step_tag(it, 1) + lane_tag, key_lane + 16);
-    mfmas(buf, 3, acc_b, kss_b);
-    epilogue(masked_c, acc_a, kss_a, step_tag(it, 2) + lane_tag, key_lane + 32);
-    if (it + 1 < ntiles) {
+    kss_b = kss_n;
+    mfmas(an, acc_b);
+    if (more) {
       lds_barrier();   // done with tile it; tile it + 1 has landed
-      mfmas((it + 1) % kFiltBufs, 0, acc_a, kss_a);
+      rd((it + 1) % kFiltBufs, 0, an, kss_n);
+    }
+    epilogue(masked_c, acc_a, kss_a, step_tag(it, 2) + lane_tag, key_lane + 32);
+    if (more) {
+      kss_a = kss_n;
+      mfmas(an, acc_a);
+      rd((it + 1) % kFiltBufs, 1, an, kss_n);
     }
     epilogue(masked_c, acc_b, kss_b, step_tag(it, 3) + lane_tag, key_lane + 48);
   };
