@@ -370,6 +370,34 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   }
 }
 
+// Eight transposed reads for the whole-line tile layout of the MLA kernel:
+// value subtile d of key subtile 0 at LDS address a[d], of key subtile 1 at
+// a[d] + HI (the per-lane row swizzle permutes the subtiles' positions, so
+// each takes its own address).  Same asm discipline as lds_read_vt4.
+template <int HI>
+__device__ __forceinline__ void lds_read_vt4_at(const uint32_t (&a)[4], v8s* av) {
+  v2i r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(HI)
+      : "memory");
+  const v2i lo[4] = {r0, r1, r2, r3}, hi[4] = {r4, r5, r6, r7};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const v4s l = __builtin_bit_cast(v4s, lo[d]), h = __builtin_bit_cast(v4s, hi[d]);
+    av[d] = (v8s){l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+  }
+}
+
 // ---- MLA shape, shared latent row: two wave groups in ping-pong -----------
 // 128 heads, key = the 576-wide latent row, value = its first 512 columns.
 // Eight waves, two per SIMD (wave w runs on SIMD w % 4), in two groups
@@ -385,11 +413,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
 // 2j into the third buffer and awaits it at the end of slot 2j+1.  P^T and
 // the rescale factors are double buffered by tile parity.
 //
-// Tile layout (unswizzled): fragment (ks, q) holds chunks 4q .. 4q+3 of
-// rows 16ks .. 16ks+15, slot = 16 (X % 4) + row % 16, so lane l of an S^T
-// operand read takes 16 bytes at 16 l (the conflict-free ds_read_b128
-// pattern); the transposed V^T reads are then 2-way conflicted, but they
-// are an eighth of the LDS read traffic.
+// Tile layout (whole lines): the 32 rows x 9 lines of 128 bytes arrive as 36
+// copies of 1 KB; copy 9 rb + L holds line L (chunks 8L .. 8L+7) of rows
+// 8 rb .. 8 rb + 7, row r % 8 in slots 8 (r % 8) .. +7 with chunk x in slot
+// position (x % 8) ^ ((r >> 1) & 7).  Every copy reads whole cache lines
+// (a gather of random 1152-byte rows into LDS moves 7.2 TB/s this way
+// against 5.3 TB/s for copies of half lines), the 16 lanes of an S^T
+// operand read hit 16 distinct bank groups, and the transposed V^T reads
+// are 2-way conflicted (an eighth of the LDS read traffic).
 constexpr int kMlaTile = 32 * (576 / 8) * 16;         // 32 latent rows, 36 KB
 constexpr size_t kMlaFixedLds = 3 * kMlaTile + 2 * 8 * 1024;
 
@@ -441,21 +472,20 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
   const uint32_t ldk = (uint32_t)(a.ld_kv * 2);  // bytes; rows * ld * 2 < 4 GiB (checked by the launcher)
   const char* kvq = (const char*)a.kv + row.base * (int64_t)ldk;
 
-  // gather (group 1): copy i of wave 4 + gw fills fragment f = 4i + gw;
-  // lane l brings chunk 4q + l/16 of row 16ks + l%16 to slot l
-  const uint32_t lofs = 16u * (uint32_t)(lane >> 4);
+  // gather (group 1): wave 4 + gw copies rows 8 gw .. 8 gw + 7 of the tile,
+  // line by line; lane l brings chunk 8L + ((l % 8) ^ swz) of row
+  // 8 gw + l / 8 to slot l of copy 9 gw + L
+  const uint32_t gsw = 16u * (uint32_t)((lane & 7) ^ ((4 * gw + (lane >> 4)) & 7));
   auto issue_tile = [&](int jl) {
     const int j0 = kbeg + jl * NK;
-    char* dst = smem + (jl % 3) * kMlaTile;
-    const int ja = j0 + c, jb = j0 + 16 + c;
-    const uint32_t ra = (uint32_t)sidx[ja < n ? ja : j0], rb = (uint32_t)sidx[jb < n ? jb : j0];
+    char* dst = smem + (jl % 3) * kMlaTile + 9 * 1024 * gw;
+    const int jr = j0 + 8 * gw + (lane >> 3);
+    const uint32_t rr = (uint32_t)sidx[jr < n ? jr : j0];
+    const char* src0 = kvq + (rr * ldk + gsw);
 #pragma unroll
-    for (int i = 0; i < 2 * VF / 4; ++i) {
-      const int f = 4 * i + gw;
-      const int ks = f >= VF ? 1 : 0, q = f - VF * ks;
-      const char* src = kvq + 64 * q + ((ks ? rb : ra) * ldk + lofs);
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)((lds_char*)dst + f * 1024), 16, 0,
+    for (int L = 0; L < 9; ++L) {
+      __builtin_amdgcn_global_load_lds((const void*)(src0 + 128 * L),
+                                       (__attribute__((address_space(3))) void*)((lds_char*)dst + L * 1024), 16, 0,
                                        0);
     }
   };
@@ -475,8 +505,15 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
   float m_run = -INFINITY, l_part = 0.f;
   const float zs = a.scale * kLog2e;
   // V^T reads: lane (sl, G') reads row 4G' + sl/4 (+16 for key subtile 1),
-  // value columns 16D + 4(sl%4) .. +3: chunk 2D + (sl%4)/2, half sl%2
-  const int vbase = ((((lane & 3) >> 1) * 16) + (4 * (lane >> 4) + ((lane & 15) >> 2))) * 16 + (lane & 1) * 8;
+  // value columns 64w + 16d + 4(sl%4) .. +3: chunk 8w + 2d + (sl%4)/2, half
+  // sl%2, found at copy 9 (G'/2) + w, slot 8 (4 (G'&1) + sl/4) + position
+  // 2 (d ^ G') + ((sl%4)/2 ^ sl/8), so subtile d sits at offset vq ^ 32 d
+  const int vq = 9216 * (lane >> 5) + 1024 * w + 128 * (4 * ((lane >> 4) & 1) + ((lane & 15) >> 2)) +
+                 16 * (((lane & 3) >> 1) ^ ((lane & 15) >> 3)) + 8 * (lane & 1) + 32 * (lane >> 4);
+  // S^T reads: lane (g, c) takes chunk 4 kk + g of row 16 ks + c, at offset
+  // sb0 + 1024 (kk / 2) + 18432 ks for even kk and sb0 ^ 64 for odd kk
+  const int sswz = (c >> 1) & 7;
+  const int sb0 = 9216 * (c >> 3) + 128 * (c & 7) + 16 * (g ^ (sswz & 3)) + 64 * (sswz >> 2);
 
   // S^T = K . Q^T for the wave's 16 heads (key subtiles 0 and 1, even and
   // odd k-steps in separate accumulators), then the online softmax in the
@@ -495,15 +532,17 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
     v8s k0[KK], k1[KK];
 #pragma unroll
     for (int kk = 0; kk < D; ++kk) {
-      k0[kk] = *(const v8s*)(tb + (kk * 64 + lane) * 16);
-      k1[kk] = *(const v8s*)(tb + ((VF + kk) * 64 + lane) * 16);
+      const char* kp = tb + ((kk & 1) ? (sb0 ^ 64) : sb0) + 1024 * (kk >> 1);
+      k0[kk] = *(const v8s*)kp;
+      k1[kk] = *(const v8s*)(kp + 18432);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (kk + D < KK) {
-        k0[kk + D] = *(const v8s*)(tb + ((kk + D) * 64 + lane) * 16);
-        k1[kk + D] = *(const v8s*)(tb + ((VF + kk + D) * 64 + lane) * 16);
+        const char* kp = tb + (((kk + D) & 1) ? (sb0 ^ 64) : sb0) + 1024 * ((kk + D) >> 1);
+        k0[kk + D] = *(const v8s*)kp;
+        k1[kk + D] = *(const v8s*)(kp + 18432);
       }
       sc0 = mfma_bf16_16x16x32(k0[kk], qf[kk], sc0);
       sc1 = mfma_bf16_16x16x32(k1[kk], qf[kk], sc1);
@@ -561,7 +600,12 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
       }
     }
     v8s av[ND];
-    lds_read_vt4<VF * 1024>(tb + vbase + 2048 * w, av);
+    {
+      const uint32_t tba = (uint32_t)(uintptr_t)(const lds_char*)tb;
+      const uint32_t va[4] = {tba + (uint32_t)vq, tba + (uint32_t)(vq ^ 32), tba + (uint32_t)(vq ^ 64),
+                              tba + (uint32_t)(vq ^ 96)};
+      lds_read_vt4_at<18432>(va, av);
+    }
 #pragma unroll
     for (int hs = 0; hs < 8; ++hs) {
       const v8s pf = *(const v8s*)(pbuf + ((par * 8 + hs) * 64 + lane) * 16);
