@@ -76,6 +76,32 @@ def load_traffic(kernel, sha):
     return e.get("bytes_per_launch")
 
 
+def source_tree_sha():
+    """Hash of every kernel and library source (any change invalidates the
+    committed per-kernel profile)."""
+    d = os.path.join(ROOT, "sparse_attention_long_indexer_amd", "csrc")
+    return kernel_source_sha(sorted(f for f in os.listdir(d) if f.endswith((".hip", ".h", ".cpp"))))
+
+
+def load_kernel_breakdown(workload):
+    """Per-kernel average durations of one workload from the committed
+    rocprofv3 kernel trace (profiles/kernel_times.json), each with its
+    algorithmic work and roofline fraction where one applies; None once any
+    library source has changed since the trace was taken."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_sha") != source_tree_sha():
+        return None
+    w = d.get("workloads", {}).get(workload)
+    if w is None:
+        return None
+    return {"source": "profiles/kernel_times.json (rocprofv3 kernel trace of this source tree)",
+            "clocks_mhz": d.get("clocks_mhz"), "kernels": w}
+
+
 def gpu_clocks():
     """Shader and memory clocks and power of GPU 0 as the system tools report
     them (amd-smi, else rocm-smi); the raw fields are kept as reported."""
@@ -666,6 +692,8 @@ def main():
         "roofline": line["roofline"], "roofline_indexer": line["roofline_indexer"],
         "measured_peaks": peaks, "clocks": clocks,
     }
+    if args.dynamic_theta is None:
+        result["roofline_indexer"]["kernels"] = load_kernel_breakdown(spec.name)
     if args.dynamic_theta is not None:
         result["metric"] = "DSA prefill tokens/s at L=128K, dynamic k (theta, k_min .. 2048)"
         result["config"]["dynamic_k"] = {"theta": args.dynamic_theta, "k_min": args.dynamic_kmin,
@@ -691,6 +719,7 @@ def main():
         if peaks:
             r = result["decode"]["roofline"]
             r["frac_measured_peak"] = round(r["achieved"] / peaks["hbm_read_gbps"], 4)
+        result["decode"]["kernels"] = load_kernel_breakdown(gen.DECODE_64.name)
         log(f"decode cold {result['decode']['ms_per_step']:.3f} ms/step, "
             f"warm {result['decode']['warm']['ms_per_step']:.3f} ms/step")
 
@@ -769,7 +798,7 @@ def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, d
                 "ms": round(idx_ms, 3), "fold_ms": round(fold_ms, 3), "scores_and_select_ms": round(idx_ms - fold_ms, 3),
                 "achieved": round(idx_tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(idx_tf / PEAK_FP8_TFLOPS, 4), "algorithmic_flops": ifl,
-                "note": "per-kernel times of the stage are in the committed rocprofv3 kernel trace"}
+                "note": "step minus attention, timed live; per-kernel times under 'kernels' (committed trace)"}
     if peaks:
         roof["frac_measured_peak"] = round(achieved / peaks["bf16_tflops"], 4)
         roof_idx["frac_measured_peak"] = round(idx_tf / peaks["fp8_tflops"], 4)
