@@ -16,8 +16,9 @@ The dominant kernel's duration is measured live with HIP events on the stream
 the kernel runs on; its roofline uses algorithmic FLOPs (or bytes) only, and
 is stated against both the published peak and the peak measured in the same
 run by the probe library (an MFMA issue loop and a streaming HBM read).  GPU
-clocks and power are read before and after the timed region.  The 8K and 32K
-prefills are timed as extra lines; decode is timed warm (one cache set) and
+clocks and power are read before, during (sampled while the timed steps
+run) and after the timed region.  The 8K and 32K prefills are timed as extra
+lines; decode is timed warm (one cache set) and
 cold (four cache sets in rotation, 24 GB, far past the 256 MB last-level
 cache).  The CPU baseline times the fp64 oracle on a stratified sample of
 query rows of the same workload with one single-threaded worker process per
@@ -134,8 +135,46 @@ def gpu_clocks():
                     flat[key] = v
         walk(d, "")
         if flat:
-            return {"tool": cmd[0], "fields": dict(list(flat.items())[:40])}
+            return {"tool": cmd[0], **clock_summary(flat)}
     return None
+
+
+def clock_summary(flat):
+    """Shader clocks (MHz, per XCD), memory clock (MHz) and socket power (W)
+    picked out of the tool's flattened fields."""
+    gfx, mem, power = [], None, None
+    for k, v in flat.items():
+        low = k.lower()
+        if not isinstance(v, (int, float)):
+            continue
+        if "gfx_" in low and low.endswith("clk.value") and "min_clk" not in low and "max_clk" not in low:
+            gfx.append(v)
+        elif ("mem_0" in low or "mclk" in low) and low.endswith("clk.value") and "min" not in low and "max" not in low:
+            mem = v
+        elif "socket_power.value" in low:
+            power = v
+    return {"gfx_mhz": gfx, "mem_mhz": mem, "power_w": power}
+
+
+class ClockSampler:
+    """Reads the clocks once on a helper thread while the GPU runs queued
+    work (the host is blocked in a synchronisation meanwhile)."""
+
+    def __init__(self):
+        import threading
+        self.result = None
+        self.t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        self.result = gpu_clocks()
+
+    def start(self):
+        self.t.start()
+        return self
+
+    def join(self):
+        self.t.join(timeout=60)
+        return self.result
 
 
 def probe_peaks(torch, dev):
@@ -679,6 +718,7 @@ def main():
     clocks = {"before": gpu_clocks()}
     line, idx, out = time_prefill(B, torch, dev, spec, x, args.steps, args.warmup, peaks,
                                   dyn_theta=args.dynamic_theta, dyn_k_min=args.dynamic_kmin, keep=True)
+    clocks["during"] = line.pop("clocks_during", None)
     clocks["after"] = gpu_clocks()
     pairs = line["roofline"]["selected_pairs"]
     result = {
@@ -755,8 +795,10 @@ def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, d
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
+    sampler = ClockSampler().start() if keep else None   # while the queued steps run
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
+    clocks_during = sampler.join() if sampler else None
     log(f"{spec.name}: prefill {dt * 1e3:.2f} ms/step, {L / dt:.4g} tokens/s")
     del ws
 
@@ -806,6 +848,8 @@ def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, d
         f"(fold {fold_ms:.3f} ms)")
     line = {"tokens_per_s": round(L / dt, 1), "ms_per_step": round(dt * 1e3, 3), "L": L, "topk": k,
             "heads": spec.H, "dk": spec.Dk, "dv": spec.Dv, "roofline": roof, "roofline_indexer": roof_idx}
+    if clocks_during is not None:
+        line["clocks_during"] = clocks_during
     if keep:
         return line, idx, out
     del idx, out
