@@ -304,59 +304,77 @@ __global__ __launch_bounds__(256) void idx_refine_kernel(const uint8_t* __restri
 // ---- 2. filter pass ---------------------------------------------------------
 constexpr int kFiltKeys = 64;             // keys per LDS tile
 constexpr int kFiltRows = 256;            // queries per block (64 per wave)
-constexpr int kSets = 2;                  // key chunks per row (long rows split in two)
+constexpr int kSetsMax = 8;               // key chunks per row (survivor sets), at most
 constexpr int kSlack = 16;                // sink slots past kCap (one tile's worth per lane)
 constexpr int kSegStride = kCap + kSlack;
 
-// Work items: long row blocks (keys past the chunk boundary kmax) are split
-// into chunk 0 = keys [0, kmax) and chunk 1 = keys [kmax, end), each with its
-// own survivor set, so no item scans more than kmax keys.  Items are ordered
-// longest first.  Row block rb holds rows [256 rb, 256 rb + 256) at
-// positions p0 + row (p0 = S - T) and sees keys [0, min(S, p0 + 256 (rb+1))).
+// Work items: the keys are cut into ns chunks of kmax keys (a multiple of
+// 256, kmax >= S / ns; ns = 2, 4 or 8, more for fewer row blocks, so that
+// short prefills still fill the chip while long ones keep few survivor sets
+// open per row); row block rb (rows [256 rb, 256 rb + 256) at
+// positions p0 + row, p0 = S - T, seeing keys [0, end_rb) with end_rb =
+// min(S, p0 + 256 (rb+1))) has one item per chunk it reaches, each with its
+// own survivor set, so no item scans more than kmax keys and short prefills
+// Items run in this order: the full chunks (chunk c
+// of every row block that reaches chunk c + 1, c ascending, row blocks
+// descending), then each row block's last, partial chunk (row blocks
+// descending).  The last-chunk item of a row block also clears the counts
+// of the sets its rows do not reach.
 struct FilterItem {
   int64_t rb;    // row block
   int set;       // key chunk / survivor set
+  int nsets;     // chunks row block rb reaches
   int64_t k0, k1;
 };
-__host__ __device__ inline int64_t filter_kmax(int64_t S) {
-  const int64_t h = (S + 1) / 2;
+__host__ __device__ inline int filter_nsets(int64_t T, int64_t S) {
+  (void)S;
+  const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
+  return nb >= 384 ? 2 : nb >= 192 ? 4 : kSetsMax;
+}
+__host__ __device__ inline int64_t filter_kmax(int64_t T, int64_t S) {
+  const int ns = filter_nsets(T, S);
+  const int64_t h = (S + ns - 1) / ns;
   return (h + kFiltRows - 1) / kFiltRows * kFiltRows;
 }
-// first row block whose key range passes kmax
-__host__ __device__ inline int64_t filter_first_long(int64_t T, int64_t S) {
-  const int64_t kmax = filter_kmax(S), p0 = S - T;
-  return kmax >= p0 ? (kmax - p0) / kFiltRows : 0;
-}
-__device__ __forceinline__ FilterItem filter_item(int64_t id, int64_t T, int64_t S) {
+// first row block whose key range passes j kmax (nb when none does)
+__host__ __device__ inline int64_t filter_first_rb(int j, int64_t T, int64_t S) {
   const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
-  const int64_t kmax = filter_kmax(S), p0 = S - T;
-  const int64_t first_long = filter_first_long(T, S);
-  const int64_t nl = nb > first_long ? nb - first_long : 0;
+  const int64_t kmax = filter_kmax(T, S), p0 = S - T, lim = (int64_t)j * kmax;
+  if (S <= lim) return nb;
+  const int64_t r = lim >= p0 ? (lim - p0) / kFiltRows : 0;
+  return r < nb ? r : nb;
+}
+__host__ __device__ inline FilterItem filter_item(int64_t id, int64_t T, int64_t S) {
+  const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
+  const int ns = filter_nsets(T, S);
+  const int64_t kmax = filter_kmax(T, S), p0 = S - T;
   FilterItem it;
-  if (id < nl) {
-    it.rb = nb - 1 - id;
-    it.set = 0;
-  } else if (id < 2 * nl) {
-    it.rb = nb - 1 - (id - nl);
-    it.set = 1;
-  } else {
-    it.rb = nb - 1 - (id - nl);
-    it.set = 0;
+  int64_t base = 0;
+  it.rb = -1;
+  it.set = 0;
+  for (int c = 0; c + 1 < ns; ++c) {
+    const int64_t cnt = nb - filter_first_rb(c + 1, T, S);   // row blocks reaching chunk c + 1
+    if (it.rb < 0 && id < base + cnt) {
+      it.rb = nb - 1 - (id - base);
+      it.set = c;
+    }
+    base += cnt;
   }
+  const bool tail = it.rb < 0;
+  if (tail) it.rb = nb - 1 - (id - base);
   const int64_t end = min(S, p0 + (it.rb + 1) * kFiltRows);
-  if (it.rb >= first_long) {
-    it.k0 = it.set ? kmax : 0;
-    it.k1 = it.set ? end : min(end, kmax);
-  } else {
-    it.k0 = 0;
-    it.k1 = end;
-  }
+  it.nsets = (int)((end + kmax - 1) / kmax);
+  if (tail) it.set = it.nsets - 1;
+  it.k0 = (int64_t)it.set * kmax;
+  it.k1 = min(end, it.k0 + kmax);
   return it;
 }
-inline int64_t filter_items(int64_t T, int64_t S) {
+__host__ __device__ inline int64_t filter_items(int64_t T, int64_t S) {
   const int64_t nb = (T + kFiltRows - 1) / kFiltRows;
-  const int64_t first_long = filter_first_long(T, S);
-  return nb + (nb > first_long ? nb - first_long : 0);
+  const int ns = filter_nsets(T, S);
+  int64_t n = nb;
+  for (int c = 1; c < ns; ++c) n += nb - filter_first_rb(c, T, S);
+  return n;
 }
 
 // A block has kFiltWaves compute waves (64 query rows each) and one producer
@@ -504,7 +522,8 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
   // -inf), so only the threshold is tested here; a segment's survivors past
   // kCap all land in its slot kCap (never read: the count reports the
   // overflow).
-  char* const wave_seg = (char*)(cand + (Q0 * kSets + item.set) * kSeg * (int64_t)kSegStride);
+  const int ns = filter_nsets(T, S);   // survivor sets per row
+  char* const wave_seg = (char*)(cand + (Q0 * ns + item.set) * kSeg * (int64_t)kSegStride);
   const uint32_t k0 = (uint32_t)item.k0;
   auto flush = [&](uint32_t n) {
     const v4f vv = vr[(tail + lane) & (kRing - 1)];
@@ -522,7 +541,7 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
     uint32_t r = 0;
     if (np) r = atomicAdd(&rc[sg * 64 + rl], np);
     // segment (row Q0 + rl, this item's key chunk, sg) within the wave's rows
-    const uint32_t seg = (rl * (kSets * kSeg) + sg) * (uint32_t)kSegStride;
+    const uint32_t seg = (rl * (uint32_t)(ns * kSeg) + sg) * (uint32_t)kSegStride;
     const uint32_t key0 = k0 + (tag >> 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -646,7 +665,7 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
   }
   if (ptr != tail) flush(ptr - tail);
 
-  const bool two = item.rb >= filter_first_long(T, S);
+  const bool last = item.set == item.nsets - 1;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (tq[q] < 0) continue;
@@ -655,8 +674,10 @@ __global__ __launch_bounds__(kFiltThreads, 4) void idx_filter_kernel(
     // lane group g reports segment g of its rows
     if (g >= kSeg) continue;
     const uint32_t n = rc[g * 64 + rl];
-    cnt_out[(t * kSets + item.set) * kSeg + g] = n > (uint32_t)kCap ? kCap + 1 : (int)n;
-    if (!two) cnt_out[(t * kSets + 1) * kSeg + g] = 0;  // rows with one key chunk
+    cnt_out[(t * ns + item.set) * kSeg + g] = n > (uint32_t)kCap ? kCap + 1 : (int)n;
+    if (last) {  // sets of chunks this row block does not reach
+      for (int sx = item.set + 1; sx < ns; ++sx) cnt_out[(t * ns + sx) * kSeg + g] = 0;
+    }
   }
 }
 
@@ -691,6 +712,9 @@ constexpr int kSfList = 512;
 static_assert(kSfPer * kSfThreads == kSelMax, "threads must divide the survivor slots");
 static_assert(kSfBins == 4 * kSfThreads, "the bin scan gives each thread four bins");
 
+// NSEG: survivor segments per row (filter_nsets(T, S) * kSeg; the launcher
+// picks the instantiation)
+template <int NSEG>
 __global__ __launch_bounds__(kSfThreads) void idx_select_fast_kernel(
     const float* __restrict__ qs, const float* __restrict__ tau, const uint2* __restrict__ cand,
     const int32_t* __restrict__ cnt_in, int64_t T, int64_t S, int64_t topk, int32_t* __restrict__ idx_out,
@@ -722,16 +746,16 @@ __global__ __launch_bounds__(kSfThreads) void idx_select_fast_kernel(
     return;
   }
   // segment starts in the concatenation of the row's segments
-  int cb[kSets * kSeg + 1];
+  int cb[NSEG + 1];
   bool over = false;
   cb[0] = 0;
 #pragma unroll
-  for (int g = 0; g < kSets * kSeg; ++g) {
-    const int c = cnt_in[t * kSets * kSeg + g];
+  for (int g = 0; g < NSEG; ++g) {
+    const int c = cnt_in[t * NSEG + g];
     over |= c > kCap;
     cb[g + 1] = cb[g] + (c > kCap ? kCap : c);
   }
-  const int total = cb[kSets * kSeg];
+  const int total = cb[NSEG];
   const float tt = tau[t];
   if (over || total > kSelMax || (tt == -INFINITY && total != n)) {
     defer(fb);
@@ -747,13 +771,13 @@ __global__ __launch_bounds__(kSfThreads) void idx_select_fast_kernel(
     const int e = tid + kSfThreads * j;
     int g = 0, start = 0;
 #pragma unroll
-    for (int i = 1; i < kSets * kSeg; ++i)
+    for (int i = 1; i < NSEG; ++i)
       if (e >= cb[i]) {
         g = i;
         start = cb[i];
       }
     uint2 cv = make_uint2(0u, 0xFFFFFFFFu);
-    if (e < total) cv = cand[(t * kSets * kSeg + g) * (int64_t)kSegStride + (e - start)];
+    if (e < total) cv = cand[(t * NSEG + g) * (int64_t)kSegStride + (e - start)];
     const float u0 = __uint_as_float(cv.x) * qsc;
     const bool ok = e < total && (int32_t)cv.y >= 0 && (int64_t)(int32_t)cv.y < n;
     key[j] = ok ? score_key(u0 > 0.f ? u0 : 0.f) : 0u;   // 0 is below every real key
@@ -948,7 +972,7 @@ __device__ inline void select_generic_row(
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t wave_cnt[kSelWaves];
   __shared__ uint32_t s_sel[2];
-  __shared__ int s_cnt[kSets * kSeg], s_cbase[kSets * kSeg + 1];
+  __shared__ int s_cnt[kSetsMax * kSeg], s_cbase[kSetsMax * kSeg + 1];
   __shared__ int32_t s_tie[kMaxTies];
   __shared__ int s_ntie, s_bad;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -963,14 +987,15 @@ __device__ inline void select_generic_row(
   const float tt = tau[t];
   const bool bucketed = n > kSelBitmapN;
   const int nwords = bucketed ? 0 : (int)((n + 31) >> 5);
-  if (tid < kSets * kSeg) s_cnt[tid] = cnt_in[t * kSets * kSeg + tid];
+  const int nseg = filter_nsets(T, S) * kSeg;
+  if (tid < nseg) s_cnt[tid] = cnt_in[t * nseg + tid];
   if (tid == 0) s_ntie = 0;
   for (int i = tid; i < nwords; i += kSelThreads) sel[i] = 0;
   __syncthreads();
   // chunk layout: segment gq owns chunks [s_cbase[gq], s_cbase[gq+1])
   if (tid == 0) {
     int nch = 0, bad = 0, total = 0;
-    for (int gq = 0; gq < kSets * kSeg; ++gq) {
+    for (int gq = 0; gq < nseg; ++gq) {
       const int cq = s_cnt[gq];
       if (cq > kCap) bad = 1;
       const int cv = cq > kCap ? kCap : cq;
@@ -978,7 +1003,7 @@ __device__ inline void select_generic_row(
       s_cbase[gq] = nch;
       nch += (cv + kChunk - 1) / kChunk;
     }
-    s_cbase[kSets * kSeg] = nch;
+    s_cbase[nseg] = nch;
     s_bad = bad || nch > kMaxChunks || (tt == -INFINITY && total != n);
   }
   __syncthreads();
@@ -986,14 +1011,14 @@ __device__ inline void select_generic_row(
     if (tid == 0) fb[1 + atomicAdd(&fb[0], 1)] = (int32_t)t;
     return;
   }
-  const int nch = s_cbase[kSets * kSeg];
+  const int nch = s_cbase[nseg];
   // stage: one 512-byte direct-to-LDS copy (32 lanes x 16 B) per chunk;
   // reads past a segment's count stay inside its kSegStride slots
   for (int ch = 2 * w + (lane >> 5); ch < nch; ch += 2 * kSelWaves) {
     int gq = 0;
-    while (gq + 1 < kSets * kSeg && ch >= s_cbase[gq + 1]) ++gq;
+    while (gq + 1 < nseg && ch >= s_cbase[gq + 1]) ++gq;
     const int ofs = (ch - s_cbase[gq]) * kChunk;
-    const uint2* src = cand + (t * kSets * kSeg + gq) * (int64_t)kSegStride + ofs + 2 * (lane & 31);
+    const uint2* src = cand + (t * nseg + gq) * (int64_t)kSegStride + ofs + 2 * (lane & 31);
     __builtin_amdgcn_global_load_lds(
         (const void*)src,
         (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint2*)cl +
@@ -1010,7 +1035,7 @@ __device__ inline void select_generic_row(
   for (int e = tid; e < nslots; e += kSelThreads) {
     const int ch = e / kChunk;
     int gq = 0;
-    while (gq + 1 < kSets * kSeg && ch >= s_cbase[gq + 1]) ++gq;
+    while (gq + 1 < nseg && ch >= s_cbase[gq + 1]) ++gq;
     const int valid = min(kChunk, min(s_cnt[gq], kCap) - (ch - s_cbase[gq]) * kChunk);
     const uint2 cv = cl[e];
     uint32_t key = 0;
@@ -1132,8 +1157,8 @@ size_t index_select_workspace_bytes(int64_t T, int64_t S) {
   size_t b = 0;
   auto add = [&](size_t x) { b += (x + 255) / 256 * 256; };
   add((size_t)T * 4);                       // tau
-  add((size_t)T * kSets * kSeg * kSegStride * 8 + kChunk * 8);  // survivors (+ copy overrun pad)
-  add((size_t)T * kSets * kSeg * 4);                // counts
+  add((size_t)T * filter_nsets(T, S) * kSeg * kSegStride * 8 + kChunk * 8);  // survivors (+ copy overrun pad)
+  add((size_t)T * filter_nsets(T, S) * kSeg * 4);                             // counts
   add((size_t)(T + 1) * 4);                 // fallback queue
   add((size_t)(T + 1) * 4);                 // generic-select queue
   add((size_t)kFbBlocks * S * 4);           // fallback score rows
@@ -1154,8 +1179,8 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
     return q;
   };
   float* tau = (float*)take((size_t)T * 4);
-  uint2* cand = (uint2*)take((size_t)T * kSets * kSeg * kSegStride * 8 + kChunk * 8);
-  int32_t* cnt = (int32_t*)take((size_t)T * kSets * kSeg * 4);
+  uint2* cand = (uint2*)take((size_t)T * filter_nsets(T, S) * kSeg * kSegStride * 8 + kChunk * 8);
+  int32_t* cnt = (int32_t*)take((size_t)T * filter_nsets(T, S) * kSeg * 4);
   int32_t* fb = (int32_t*)take((size_t)(T + 1) * 4);
   int32_t* gq = (int32_t*)take((size_t)(T + 1) * 4);
   float* scratch = (float*)take((size_t)kFbBlocks * S * 4);
@@ -1181,8 +1206,20 @@ hipError_t launch_index_select(const uint8_t* qf, const float* qs, const uint8_t
   e = set_lds_limit_once((const void*)idx_select_generic_kernel, (int)(2 * kSelMax * 4 + (kSelBitmapN / 32) * 4),
                          attr_done);
   if (e != hipSuccess) return e;
-  idx_select_fast_kernel<<<(unsigned)T, kSfThreads, lds_fast, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, gq, fb,
-                                                                   force_fallback ? 1 : 0, dyn);
+  {
+    static_assert(kSeg == 1, "the select instantiations cover 2, 4 and 8 segments per row");
+    const int nseg = filter_nsets(T, S) * kSeg;
+    const int ff = force_fallback ? 1 : 0;
+    if (nseg == 2)
+      idx_select_fast_kernel<2><<<(unsigned)T, kSfThreads, lds_fast, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out,
+                                                                            gq, fb, ff, dyn);
+    else if (nseg == 4)
+      idx_select_fast_kernel<4><<<(unsigned)T, kSfThreads, lds_fast, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out,
+                                                                            gq, fb, ff, dyn);
+    else
+      idx_select_fast_kernel<kSetsMax * kSeg><<<(unsigned)T, kSfThreads, lds_fast, st>>>(
+          qs, tau, cand, cnt, T, S, topk, idx_out, gq, fb, ff, dyn);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned gen_blocks = (unsigned)(T < kGenericBlocks ? T : kGenericBlocks);
   idx_select_generic_kernel<<<gen_blocks, kSelThreads, lds, st>>>(qs, tau, cand, cnt, T, S, topk, idx_out, gq, fb,
