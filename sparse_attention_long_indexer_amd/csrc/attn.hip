@@ -402,8 +402,9 @@ __device__ __forceinline__ void lds_read_vt4_at(const uint32_t (&a)[4], v8s* av)
 // 128 heads, key = the 576-wide latent row, value = its first 512 columns.
 // Eight waves, two per SIMD (wave w runs on SIMD w % 4), in two groups
 // G = w / 4.  Wave w computes S^T and the softmax for heads 16w .. 16w+15
-// over all 576 key dims, and accumulates O^T for all 128 heads over value
-// columns 64w .. 64w+63.  The loop runs in slots closed by block barriers:
+// over all 576 key dims (16x16x32 MFMAs), and accumulates O^T for all 128
+// heads over value columns 64w .. 64w+63 (32x32x16 MFMAs, which one wave
+// alone issues faster than 16x16x32).  The loop runs in slots closed by block barriers:
 // in slot 2j group 0 does S^T + softmax of tile j while group 1 does PV of
 // tile j-1, in slot 2j+1 group 1 does S^T + softmax of tile j while group 0
 // does PV of tile j-1.  Each SIMD then always holds one wave feeding its
@@ -435,9 +436,7 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 
 __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int64_t* seq_off) {
   constexpr int NK = 32, DK = 576, DV = 512, H = 128, NW = 8;
-  constexpr int VF = DK / 32;       // fragments (32 dims) per 16-key subtile
   constexpr int KK = DK / 32;       // k-steps of S^T
-  constexpr int ND = DV / NW / 16;  // value subtiles per wave
   extern __shared__ __align__(16) char smem[];
   char* pbuf = smem + 3 * kMlaTile;                 // [parity][wave][lane] 16-byte P^T fragments
   int32_t* sidx = (int32_t*)(pbuf + 2 * 8 * 1024);  // the block's index row
@@ -497,19 +496,27 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v8s*)(qp + 32 * kk);
   }
-  v4f o[ND][8];
+  // O^T blocks of 32 value columns (64w + 32 vb ..) x 32 heads (32 hb ..)
+  v16f o[2][4];
 #pragma unroll
-  for (int d = 0; d < ND; ++d)
+  for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-    for (int hs = 0; hs < 8; ++hs) o[d][hs] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[vb][hb][r] = 0.f;
   float m_run = -INFINITY, l_part = 0.f;
   const float zs = a.scale * kLog2e;
-  // V^T reads: lane (sl, G') reads row 4G' + sl/4 (+16 for key subtile 1),
-  // value columns 64w + 16d + 4(sl%4) .. +3: chunk 8w + 2d + (sl%4)/2, half
-  // sl%2, found at copy 9 (G'/2) + w, slot 8 (4 (G'&1) + sl/4) + position
-  // 2 (d ^ G') + ((sl%4)/2 ^ sl/8), so subtile d sits at offset vq ^ 32 d
-  const int vq = 9216 * (lane >> 5) + 1024 * w + 128 * (4 * ((lane >> 4) & 1) + ((lane & 15) >> 2)) +
-                 16 * (((lane & 3) >> 1) ^ ((lane & 15) >> 3)) + 8 * (lane & 1) + 32 * (lane >> 4);
+  // 32x32x16 PV: A operand (value block vb, k-step m) of lane (G = l/16,
+  // s = l%16) is column 64w + 32 vb + 16 (G%2) + s of keys 4 gk .. +3 and
+  // 16 + 4 gk .. +3, gk = 2m + G/2 (the keys S^T lane (c, gk) holds); the
+  // source lane s reads row 8m + 4 (G/2) + s/4, columns .. + 4 (s%4): chunk
+  // 8w + 4 vb + 2 (G%2) + (s%4)/2, half s%2, at vqn ^ 64 (vb ^ m), + 9216 m
+  const int G16 = lane >> 4, s16 = lane & 15;
+  const int vqn = 1024 * w + 128 * (4 * (G16 >> 1) + (s16 >> 2)) +
+                  16 * (2 * ((G16 & 1) ^ (G16 >> 1)) + (((s16 & 3) >> 1) ^ (s16 >> 3))) + 8 * (s16 & 1);
+  // B operand (heads 32 hb + j, j = l%32, k-step m): the P^T fragment of
+  // S^T wave 2 hb + j/16, lane (j%16) + 16 (2m + l/32)
+  const int pq = 1024 * ((lane & 31) >> 4) + 16 * ((lane & 15) + 16 * (lane >> 5));
   // S^T reads: lane (g, c) takes chunk 4 kk + g of row 16 ks + c, at offset
   // sb0 + 1024 (kk / 2) + 18432 ks for even kk and sb0 ^ 64 for odd kk
   const int sswz = (c >> 1) & 7;
@@ -593,25 +600,29 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
     for (int i = 0; i < NW; ++i) resc |= s_need[par][i] != 0;
     if (resc) {
 #pragma unroll
-      for (int hs = 0; hs < 8; ++hs) {
-        const float cr = s_corr[par][16 * hs + c];
+      for (int hb = 0; hb < 4; ++hb) {
+        const float cr = s_corr[par][32 * hb + (lane & 31)];
 #pragma unroll
-        for (int d = 0; d < ND; ++d) o[d][hs] *= cr;
+        for (int vb = 0; vb < 2; ++vb) o[vb][hb] *= cr;
       }
     }
-    v8s av[ND];
+    v8s av[4];  // [2 m + vb]
     {
       const uint32_t tba = (uint32_t)(uintptr_t)(const lds_char*)tb;
-      const uint32_t va[4] = {tba + (uint32_t)vq, tba + (uint32_t)(vq ^ 32), tba + (uint32_t)(vq ^ 64),
-                              tba + (uint32_t)(vq ^ 96)};
+      const uint32_t va[4] = {tba + (uint32_t)vqn, tba + (uint32_t)(vqn ^ 64), tba + (uint32_t)((vqn ^ 64) + 9216),
+                              tba + (uint32_t)(vqn + 9216)};
       lds_read_vt4_at<18432>(va, av);
     }
 #pragma unroll
-    for (int hs = 0; hs < 8; ++hs) {
-      const v8s pf = *(const v8s*)(pbuf + ((par * 8 + hs) * 64 + lane) * 16);
+    for (int hb = 0; hb < 4; ++hb) {
+      const char* pb = pbuf + (par * 8 + 2 * hb) * 1024 + pq;
+      const v8s pf0 = *(const v8s*)pb;
+      const v8s pf1 = *(const v8s*)(pb + 512);
 #pragma unroll
-      for (int d = 0; d < ND; ++d) o[d][hs] = mfma_bf16_16x16x32(av[d], pf, o[d][hs]);
-      if (hs % DSA_PV_GROUP == DSA_PV_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+      for (int vb = 0; vb < 2; ++vb) o[vb][hb] = mfma_bf16_32x32x16(av[vb], pf0, o[vb][hb]);
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) o[vb][hb] = mfma_bf16_32x32x16(av[2 + vb], pf1, o[vb][hb]);
+      if (hb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -659,11 +670,15 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
   __syncthreads();
   if (partial) {
 #pragma unroll
-    for (int hs = 0; hs < 8; ++hs) {
-      const int h = 16 * hs + c;
-      float* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + 64 * w;
+    for (int hb = 0; hb < 4; ++hb) {
+      const int h = 32 * hb + (lane & 31);
+      float* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + 64 * w + 4 * (lane >> 5);
 #pragma unroll
-      for (int d = 0; d < ND; ++d) *(v4f*)(op + 16 * d + 4 * g) = o[d][hs];
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *(v4f*)(op + 32 * vb + 8 * rq) =
+              (v4f){o[vb][hb][4 * rq], o[vb][hb][4 * rq + 1], o[vb][hb][4 * rq + 2], o[vb][hb][4 * rq + 3]};
     }
     return;
   }
@@ -674,18 +689,20 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const int hs = 4 * half + hh;
-      const float l = s_l[16 * hs + c];
+    for (int hh = 0; hh < 2; ++hh) {
+      const int hb = 2 * half + hh;
+      const float l = s_l[32 * hb + (lane & 31)];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      char* sp_row = smem + (16 * hh + c) * kRow + (64 * w + 4 * g) * 2;
+      char* sp_row = smem + (32 * hh + (lane & 31)) * kRow + (64 * w + 4 * (lane >> 5)) * 2;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        v2i pk;
-        pk[0] = (int)pack_bf16x2(o[d][hs][0] * inv, o[d][hs][1] * inv);
-        pk[1] = (int)pack_bf16x2(o[d][hs][2] * inv, o[d][hs][3] * inv);
-        *(v2i*)(sp_row + 32 * d) = pk;
-      }
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          v2i pk;
+          pk[0] = (int)pack_bf16x2(o[vb][hb][4 * rq] * inv, o[vb][hb][4 * rq + 1] * inv);
+          pk[1] = (int)pack_bf16x2(o[vb][hb][4 * rq + 2] * inv, o[vb][hb][4 * rq + 3] * inv);
+          *(v2i*)(sp_row + 2 * (32 * vb + 8 * rq)) = pk;
+        }
     }
     lds_barrier();
     // 64 rows x 64 lanes of 16 bytes: wave w writes rows w, w + 8, ...

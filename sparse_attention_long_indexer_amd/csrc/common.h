@@ -116,6 +116,13 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8s& a, const v8s& b, co
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16((v8bf)a, (v8bf)b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 -> fp32; lane l supplies 8 values of row / column (l % 32)
+// for reduction slice l / 32; result register r of lane l holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4 of column l % 32.
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const v8s& a, const v8s& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16((v8bf)a, (v8bf)b, c, 0, 0, 0);
+}
+
 // ---- wave helpers --------------------------------------------------------
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
