@@ -142,10 +142,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   constexpr int LOADS = (NFRAG + NW - 1) / NW;  // fragment copies per wave per tile
   constexpr int VF = VCH / 4;
   constexpr int KKW = DK / 32;  // k-steps of 32 dims
-  // dynamic LDS: [2][TILE_BYTES] tiles | [NW] P^T fragments (1 KB) | index row
+  // dynamic LDS: [2][TILE_BYTES] tiles | [NW] P^T fragments (1 KB) | [3][32]
+  // index entries of the upcoming tiles (copied from the index row two
+  // tiles ahead), which keeps a one-wave block at 33 KB
   extern __shared__ __align__(16) char smem[];
   char* pbuf = smem + 2 * TILE_BYTES;
-  int32_t* sidx = (int32_t*)(pbuf + NW * 1024);
+  int32_t* sring = (int32_t*)(pbuf + NW * 1024);
   __shared__ float s_corr[H], s_l[H];
   __shared__ int s_need[NW];
   __shared__ int s_cnt;
@@ -156,16 +158,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   const int64_t t = blockIdx.x / a.splits;
   const int sp = (int)(blockIdx.x % a.splits);
   const AttnRow row = attn_row(a, seq_off, t);
-  // stage the query's index row; n = leading valid entries
+  // n = leading valid entries of the query's index row
   if (tid == 0) s_cnt = (int)a.k;
   __syncthreads();
   {
     int first = (int)a.k;
-    for (int j = tid; j < (int)a.k; j += NT) {
-      int32_t s = row.ip[j];
-      if (s < 0 && j < first) first = j;
-      sidx[j] = s < row.len ? s : (int32_t)(row.len - 1);
-    }
+    for (int j = tid; j < (int)a.k; j += NT)
+      if (row.ip[j] < 0 && j < first) first = j;
     if (first < (int)a.k) atomicMin(&s_cnt, first);
   }
   __syncthreads();
@@ -186,11 +185,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   // is wave-uniform (a wave past the last fragment skips the copy)
   const int rl = (lane & 15) ^ ((lane & 16) >> 1);
   const uint32_t lofs = 16u * (uint32_t)(lane >> 4);
+  // wave 0 copies a tile's 32 index entries into ring slot tile % 3
+  auto fetch_idx = [&](int tile) {
+    if (w == 0 && lane < NK) {
+      const int j = min(tile * NK + lane, (int)a.k - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(row.ip + j),
+                                       (__attribute__((address_space(3))) void*)(lds_char*)(sring + (tile % 3) * NK),
+                                       4, 0, 0);
+    }
+  };
+  const int32_t lenm1 = (int32_t)(row.len - 1);
   auto issue_tile = [&](int tile) {
     const int j0 = tile * NK;
     char* dst = smem + (tile & 1) * TILE_BYTES;
-    const int ja = j0 + rl, jb = j0 + 16 + rl;
-    const uint32_t sa = (uint32_t)sidx[ja < n ? ja : j0], sb = (uint32_t)sidx[jb < n ? jb : j0];
+    // past the valid entries: the tile's first one (valid); an index past
+    // the query's rows reads its last row
+    const int32_t* si = sring + (tile % 3) * NK;
+    const int32_t ra = si[j0 + rl < n ? rl : 0], rb = si[j0 + 16 + rl < n ? 16 + rl : 0];
+    const uint32_t sa = (uint32_t)(ra < lenm1 ? ra : lenm1), sb = (uint32_t)(rb < lenm1 ? rb : lenm1);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + w;
@@ -237,12 +249,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   // reading before the barrier that closed the previous tile.
   const int t0 = kbeg / NK;  // first tile of this split
   if (ntiles > 0) {
+    fetch_idx(t0);
+    if (ntiles > 1) fetch_idx(t0 + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     issue_tile(t0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   for (int it = t0; it < t0 + ntiles; ++it) {
     if (it + 1 < t0 + ntiles) issue_tile(it + 1);
+    // into the slot of tile it - 1, whose gather every wave issued two
+    // barriers ago; it lands with the gather, before the tile's end
+    if (it + 2 < t0 + ntiles) fetch_idx(it + 2);
     const char* tb = smem + (it & 1) * TILE_BYTES;
     const int j0 = it * NK;
     // S^T = K . Q^T (key subtiles ks = rows 16ks + c)
@@ -843,10 +862,10 @@ bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int
   if (H == 16 && Dk == 128 && Dv == 128) return true;
   if (H == 128 && Dk == 576 && Dv == 512) {
     // shared latent row: three gathered tiles + two P^T sets + the index
-    // row; separate V: two tiles of key and value rows + P^T + the index row
+    // row; separate V: two tiles of key and value rows + P^T + index ring
     if (!sep_v) return kMlaFixedLds + (size_t)k * 4 <= kAttnLdsLimit;
     const size_t tile = (size_t)32 * (Dk / 8 + Dv / 8) * 16;
-    return 2 * tile + 8 * 1024 + (size_t)k * 4 <= kAttnLdsLimit;
+    return 2 * tile + 8 * 1024 + 3 * 32 * 4 <= kAttnLdsLimit;
   }
   return false;
 }
@@ -873,13 +892,10 @@ size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t 
 template <int DK, int DV, int NW, bool SEPV>
 static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
   constexpr size_t tile = (size_t)32 * (DK / 8 + (SEPV ? DV / 8 : 0)) * 16;
-  constexpr size_t fixed = 2 * tile + (size_t)NW * 1024;
-  constexpr size_t lds_max = fixed + (size_t)DSA_MAX_TOPK * 4 <= kAttnLdsLimit
-                                 ? fixed + (size_t)DSA_MAX_TOPK * 4 : kAttnLdsLimit;
-  const size_t lds = fixed + (size_t)a.k * 4;
-  if (lds > lds_max) return hipErrorInvalidValue;
+  constexpr size_t lds = 2 * tile + (size_t)NW * 1024 + 3 * 32 * 4;
+  static_assert(lds <= kAttnLdsLimit, "two tiles, the P^T fragments and the index ring fit in LDS");
   static std::atomic<uint64_t> attr_done{0};
-  hipError_t ea = set_lds_limit_once((const void*)attn_bf16_kernel<DK, DV, NW, SEPV>, (int)lds_max, attr_done);
+  hipError_t ea = set_lds_limit_once((const void*)attn_bf16_kernel<DK, DV, NW, SEPV>, (int)lds, attr_done);
   if (ea != hipSuccess) return ea;
   attn_bf16_kernel<DK, DV, NW, SEPV><<<(unsigned)(a.T * a.splits), NW * 64, lds, st>>>(a, seq_off);
   hipError_t e = hipGetLastError();
