@@ -176,9 +176,8 @@ dsa_status_t dsa_topk_dynamic(const float* scores, int64_t ld, int64_t T, int64_
  * out       device [T][H][Dv] (dtype)
  * lse_out   device fp32 [T][H] (natural log of sum_s exp(z_s)) or NULL
  * Supported (dtype, H, Dk, Dv): (F32, any H <= 64, Dk, Dv <= 128 and
- * multiples of 4), (BF16, 16, 128, 128), (BF16, 128, 576, 512); the last
- * with a separate V pointer takes k <= 3584 (its gathered tiles fill LDS).
- * BF16 also needs S * max(ld_kv, ld_v) * 2 <= 4 GiB (rows are addressed by
+ * multiples of 4), (BF16, 16, 128, 128), (BF16, 128, 576, 512), with or
+ * without a separate V pointer.  BF16 also needs S * max(ld_kv, ld_v) * 2 <= 4 GiB (rows are addressed by
  * 32-bit byte offsets); otherwise DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_sparse_attn_workspace_size(int64_t T, int64_t H, int64_t Dv, int64_t k, dsa_dtype_t dtype);

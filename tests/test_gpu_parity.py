@@ -142,6 +142,7 @@ def test_topk_bit_exact(dev, T, S, k, levels):
 ATTN_CASES = [
     ("f32_h4_d64", gen.TINY_F32.with_(L=300), 64),
     ("bf16_h16_d128", gen.PREFILL_8K.with_(L=3000), 2048),
+    ("bf16_h16_k4096", gen.PREFILL_8K.with_(L=5000), 4096),
     ("bf16_mla", gen.PREFILL_32K.with_(L=2500), 2048),
     ("bf16_mla_unit", gen.PREFILL_32K.with_(L=2500, qkv_unit=True), 700),
     ("bf16_mla_k4096", gen.PREFILL_32K.with_(L=5000), 4096),      # the largest k
@@ -217,16 +218,17 @@ def test_sparse_attn_mla_rescale_and_ragged(dev, T):
     say("rows", len(rows), "worst", worst)
 
 
-def test_sparse_attn_separate_v_view(dev):
+@pytest.mark.parametrize("L,k", [(600, 256), (5000, 4096)], ids=["k256", "k4096"])
+def test_sparse_attn_separate_v_view(dev, L, k):
     """The latent-row reading (V = first Dv entries of the KV row, taken by
     the two-group MLA kernel) and the same columns passed as an explicit V
     with its own leading dimension (the separate-V kernel) both match the
     oracle, and agree with each other to one bf16 rounding: the two kernels
     accumulate in different orders, so their fp32 results differ far below
     a bf16 unit in the last place (2^-7 relative)."""
-    spec = gen.PREFILL_32K.with_(L=600)
+    spec = gen.PREFILL_32K.with_(L=L)
     x = gen.make_prefill(spec, seed=6, device=dev)
-    idx = gen.make_selection(16, spec.L, 256, seed=7, min_valid=1).to(dev)
+    idx = gen.make_selection(16, spec.L, k, seed=7, min_valid=1).to(dev)
     q = x["q"][:16].contiguous()
     a = B.dsa_sparse_attn(q, x["kv"], idx, spec.scale, v=None, Dv=512)
     b = B.dsa_sparse_attn(q, x["kv"], idx, spec.scale, v=x["kv"][:, :512], Dv=512)
