@@ -9,7 +9,7 @@
  * Pointers are device memory owned by the caller.
  *
  * dsa_probe_mfma: `blocks` workgroups of 256 threads; every wave issues
- *   `iters` rounds of 8 independent matrix instructions of `kind`:
+ *   `iters` (even) rounds of 8 independent matrix instructions of `kind`:
  *     0  v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3 x e4m3, 65536 FLOP each)
  *     1  v_mfma_f32_16x16x32_bf16  (16384 FLOP each)
  *     2  v_mfma_f32_32x32x16_bf16  (32768 FLOP each)

@@ -39,9 +39,14 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int64_t iters, float* _
     v4f acc[kChains];
 #pragma unroll
     for (int c = 0; c < kChains; ++c) acc[c] = (v4f){0.f, 0.f, 0.f, 0.f};
-    for (int64_t it = 0; it < iters; ++it) {
+    // two MFMAs per chain per iteration (the accumulators then keep their
+    // registers across the loop; with one, the compiler rotated them through
+    // register copies that wait on every result)
+    for (int64_t it = 0; it < iters; it += 2) {
 #pragma unroll
-      for (int c = 0; c < kChains; ++c) acc[c] = mfma_bf16_16x16x32(a, b, acc[c]);
+      for (int c = 0; c < kChains; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[c] = mfma_bf16_16x16x32(a, b, acc[c]);
     }
 #pragma unroll
     for (int c = 0; c < kChains; ++c) r += acc[c][0] + acc[c][3];
@@ -104,7 +109,7 @@ double dsa_probe_mfma_flops(int kind, int64_t iters, int64_t blocks) {
 }
 
 int dsa_probe_mfma(int kind, int64_t iters, int64_t blocks, float* sink, void* stream) {
-  if (kind < 0 || kind > 2 || iters < 0 || blocks < 1 || blocks > 2147483647 || !sink) return -1;
+  if (kind < 0 || kind > 2 || iters < 0 || (iters & 1) || blocks < 1 || blocks > 2147483647 || !sink) return -1;
   hipStream_t st = (hipStream_t)stream;
   if (kind == 0) probe_mfma_kernel<0><<<(unsigned)blocks, 256, 0, st>>>(iters, sink);
   else if (kind == 1) probe_mfma_kernel<1><<<(unsigned)blocks, 256, 0, st>>>(iters, sink);

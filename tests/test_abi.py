@@ -49,6 +49,7 @@ def test_probe_library_exports(lib):
     probe.dsa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     assert probe.dsa_probe_mfma(7, 10, 2, _vp(), None) == -1
     assert probe.dsa_probe_mfma(0, 10, 2, None, None) == -1
+    assert probe.dsa_probe_mfma(1, 11, 2, _vp(), None) == -1   # odd round count
     probe.dsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_void_p]
     assert probe.dsa_probe_read(_vp(), 4096 * 3 + 8, 1, _vp(), None) == -1     # not a multiple of 16
