@@ -3,25 +3,26 @@
 // selected keys, all query heads sharing one key/value head as in MLA's MQA
 // mode).
 //
-// Two bf16 kernels.  The MLA shape with the shared latent row (128 heads,
+// Three bf16 kernels.  The MLA shape with the shared latent row (128 heads,
 // key = 576-wide latent row, value = its first 512 columns) runs
 // attn_mla_kernel, where two groups of four waves alternate between S^T +
 // softmax and PV so that each SIMD always has one wave feeding its matrix
-// core (described at the kernel).  The other shapes (16 heads of 128, and
-// MLA with a separate value tensor) run attn_bf16_kernel: one block per
-// query (or per key split of one), 16 heads per wave.  Per tile of 32
-// selected keys the block gathers the rows into LDS with direct-to-LDS
-// copies (double buffered: the gather of tile i+1 runs during tile i), then
+// core.  16 heads of 128 run attn_h16_kernel: one wave per query over
+// 16-key tiles, P^T kept in registers, nine blocks per CU.  MLA with a
+// separate value tensor runs attn_bf16_kernel: one block per query (or per
+// key split of one), 16 heads per wave.  Each kernel gathers the selected
+// rows into LDS with direct-to-LDS copies (the gather of the next tile runs
+// during the current one), then
 //   S^T = K . Q^T   with v_mfma_f32_16x16x32_bf16 (A = K fragments from LDS,
 //                   B = Q^T held in registers for the whole loop),
-//   an online softmax per head in the log2 domain, P^T to LDS, and
-//   O^T += V^T . P^T per wave for all heads over its own slice of the value
+//   an online softmax per head in the log2 domain, and
+//   O^T += V^T . P^T for all heads over the wave's slice of the value
 //                   columns (A = V^T via transposed LDS reads, B = P^T).
 // Heads sit in the N dimension, one head per lane column, so the softmax
-// rescale of O is a per-lane scalar.  Barriers inside the loop order LDS
-// only; the gather is awaited explicitly at the end of each tile.  With few
-// queries (batched decode) the selected keys are split over blocks and an
-// LSE combine kernel merges the parts.
+// rescale of O is a per-lane scalar.  Barriers inside the loops order LDS
+// only; the gathers are awaited explicitly.  With few queries (batched
+// decode) the selected keys are split over blocks and an LSE combine kernel
+// merges the parts.  (Each kernel is described where it is defined.)
 //
 // fp32 path: a plain VALU kernel for the small fp32 configuration.
 #include "common.h"
@@ -123,6 +124,9 @@ __device__ __forceinline__ void lds_read_vt4(const char* lds_ptr, v8s* av) {
   }
 }
 
+// MLA with a separate value tensor: one block of NW waves per query (or key
+// split), wave w owning heads 16w .. 16w+15 for S^T and the softmax and
+// value columns w DV/NW .. for PV, 32-key tiles double buffered.
 template <int DK, int DV, int NW, bool SEPV>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const int64_t* seq_off) {
   constexpr int NK = 32;                        // keys per tile
@@ -414,6 +418,203 @@ __device__ __forceinline__ void lds_read_vt4_at(const uint32_t (&a)[4], v8s* av)
   for (int d = 0; d < 4; ++d) {
     const v4s l = __builtin_bit_cast(v4s, lo[d]), h = __builtin_bit_cast(v4s, hi[d]);
     av[d] = (v8s){l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+  }
+}
+
+// ---- 16 heads of 128: one wave per query, 16-key tiles ----------------------
+// S^T (16 keys x 16 heads) with 16x16x32 MFMAs over the 128 key dims; the
+// result lane (c, g) holds keys 4g .. 4g+3 of head c, which is exactly the
+// B operand of a 16x16x16 MFMA, so P^T stays in registers and O^T (128
+// value columns x 16 heads, 8 subtiles) accumulates with 16x16x16 MFMAs.
+// Every O^T entry of a lane belongs to its head c, so the rescale is
+// lane-local too.  A block holds two tiles (4 KB of key rows, plus 4 KB of
+// value rows with a separate V) and a 3-slot ring of index entries: about
+// 16 KB, so nine one-wave blocks share a CU.
+//
+// Tile layout: row r (256 bytes) at 256 r, its 16-byte chunk x in slot
+// x ^ sw(r), sw(r) = 2 (r % 8) + r / 8.  The 16 lanes of an S^T operand read
+// (chunk 4kk + g of rows 0..15) and the 32 lanes of a half-wave transposed
+// V read (rows 4G + s/4 of G = 0, 1 or 2, 3; chunks 2D, 2D + 1) each hit
+// distinct bank groups.  A 1 KB copy brings four rows, 16 lanes per row, so
+// every copy reads whole 128-byte lines.
+__device__ __forceinline__ int h16_sw(int r) { return ((r << 1) & 14) | (r >> 3); }
+
+template <bool SEPV>
+__global__ __launch_bounds__(64) void attn_h16_kernel(AttnArgs a, const int64_t* seq_off) {
+  constexpr int NK = 16, D = 128, H = 16;
+  constexpr int KB = NK * D * 2;             // 4 KB of key rows per tile
+  constexpr int TILE = SEPV ? 2 * KB : KB;
+  constexpr int KK = D / 32;                 // S^T k-steps
+  constexpr int ND = D / 16;                 // O^T value subtiles
+  extern __shared__ __align__(16) char smem[];
+  int32_t* sring = (int32_t*)(smem + 2 * TILE);   // [3][NK] index entries
+  __shared__ int s_cnt;
+
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t t = blockIdx.x / a.splits;
+  const int sp = (int)(blockIdx.x % a.splits);
+  const AttnRow row = attn_row(a, seq_off, t);
+  // n = leading valid entries of the query's index row
+  if (lane == 0) s_cnt = (int)a.k;
+  __syncthreads();
+  {
+    int first = (int)a.k;
+    for (int j = lane; j < (int)a.k; j += 64)
+      if (row.ip[j] < 0 && j < first) first = j;
+    if (first < (int)a.k) atomicMin(&s_cnt, first);
+  }
+  __syncthreads();
+  const int nvalid = s_cnt;
+  const int per = ((nvalid + a.splits - 1) / a.splits + NK - 1) / NK * NK;
+  const int kbeg = min(nvalid, sp * per);
+  const int n = min(nvalid, kbeg + per);
+  const uint32_t ldk = (uint32_t)(a.ld_kv * 2), ldv = (uint32_t)((SEPV ? a.ld_v : a.ld_kv) * 2);  // bytes
+  const char* kvq = (const char*)a.kv + row.base * (int64_t)ldk;
+  const char* vvq = SEPV ? (const char*)a.v + row.base * (int64_t)ldv : kvq;
+  const int32_t lenm1 = (int32_t)(row.len - 1);
+
+  // lanes 0..15 copy a tile's index entries into ring slot tile % 3
+  auto fetch_idx = [&](int tile) {
+    if (lane < NK) {
+      const int j = min(tile * NK + lane, (int)a.k - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(row.ip + j),
+                                       (__attribute__((address_space(3))) void*)(lds_char*)(sring + (tile % 3) * NK),
+                                       4, 0, 0);
+    }
+  };
+  // copy i brings rows 4 (i % 4) .. +3 (key rows, then value rows); lane l
+  // fills slot l % 16 of row 4 (i % 4) + l / 16 with chunk (l % 16) ^ sw(row)
+  auto issue_tile = [&](int tile) {
+    const int j0 = tile * NK;
+    char* dst = smem + (tile & 1) * TILE;
+    const int32_t* si = sring + (tile % 3) * NK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * q + g;
+      // past the valid entries: the tile's first one (valid); an index past
+      // the query's rows reads its last row
+      const int32_t e = si[j0 + r < n ? r : 0];
+      const uint32_t rr = (uint32_t)(e < lenm1 ? e : lenm1);
+      const uint32_t col = 16u * (uint32_t)(c ^ h16_sw(r));
+      __builtin_amdgcn_global_load_lds((const void*)(kvq + (rr * ldk + col)),
+                                       (__attribute__((address_space(3))) void*)((lds_char*)dst + q * 1024), 16, 0,
+                                       0);
+      if (SEPV)
+        __builtin_amdgcn_global_load_lds((const void*)(vvq + (rr * ldv + col)),
+                                         (__attribute__((address_space(3))) void*)((lds_char*)dst + KB + q * 1024),
+                                         16, 0, 0);
+    }
+  };
+
+  // Q^T fragments, dims 32kk + 8g .. +7, of head c
+  v8s qf[KK];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + (t * H + c) * (int64_t)D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const v8s*)(qp + 32 * kk);
+  }
+  v4f o[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) o[d] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+  const float zs = a.scale * kLog2e;
+  const int ntiles = (n - kbeg + NK - 1) / NK;
+  // S^T operand of k-step kk: row c, chunk 4kk + g
+  const int sw_c = h16_sw(c);
+  // V^T operand of subtile d: source lane (s = l % 16, G = l / 16) reads row
+  // 4G + s/4, value columns 16d + 4 (s%4) .. +3: chunk 2d + (s%4)/2, half s%2
+  const int vr = 4 * g + (c >> 2);
+  const int vsw = h16_sw(vr), vh = ((c & 3) >> 1);
+  const int voff = 256 * vr + 8 * (c & 1);
+
+  const int t0 = kbeg / NK;
+  const int tend = t0 + ntiles;
+  if (ntiles > 0) {
+    fetch_idx(t0);
+    if (ntiles > 1) fetch_idx(t0 + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue_tile(t0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int it = t0; it < tend; ++it) {
+    if (it + 1 < tend) issue_tile(it + 1);
+    // into the slot of tile it - 1, gathered two iterations ago
+    if (it + 2 < tend) fetch_idx(it + 2);
+    const char* tb = smem + (it & 1) * TILE;
+    const int j0 = it * NK;
+    // S^T = K . Q^T, even and odd k-steps in separate accumulators
+    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const v8s kf = *(const v8s*)(tb + 256 * c + 16 * ((4 * kk + g) ^ sw_c));
+      if (kk & 1)
+        s1 = mfma_bf16_16x16x32(kf, qf[kk], s1);
+      else
+        s0 = mfma_bf16_16x16x32(kf, qf[kk], s0);
+    }
+    // online softmax (log2 domain); the running max only moves when a tile
+    // raises it by more than 2^8, so O is rescaled rarely
+    float zt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zt[i] = (j0 + 4 * g + i < n) ? (s0[i] + s1[i]) * zs : -INFINITY;
+    float mx = fmaxf(fmaxf(zt[0], zt[1]), fmaxf(zt[2], zt[3]));
+    mx = rows_max(mx);
+    const bool need = mx > m_run + 8.f;
+    const float mnew = need ? mx : m_run;
+    const float corr = exp2f(m_run - mnew);
+    m_run = mnew;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = exp2f(zt[i] - mnew);
+    l_part = l_part * corr + ((p[0] + p[1]) + (p[2] + p[3]));
+    if (__any(need)) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) o[d] *= corr;
+    }
+    const v2i pk = {(int)pack_bf16x2(p[0], p[1]), (int)pack_bf16x2(p[2], p[3])};
+    const v4s pf = __builtin_bit_cast(v4s, pk);
+    // O^T += V^T . P^T
+    const char* vb = SEPV ? tb + KB : tb;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const v4s av = lds_read_tr16(vb, voff + 16 * ((2 * d + vh) ^ vsw));
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pf, o[d], 0, 0, 0);
+    }
+    if (it + 1 < tend) __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+  }
+
+  // epilogue: row sums per head, then lane (c, g) writes O^T[dv = 16d + 4g
+  // + i][head c]: normalised bf16 output, or with several splits the
+  // unnormalised fp32 partial plus (max, sum)
+  const bool partial = a.splits > 1;
+  const float l = rows_sum(l_part);
+  if (g == 0) {
+    if (partial) {
+      float* ml = a.part_ml + ((t * a.splits + sp) * H + c) * 2;
+      ml[0] = m_run;
+      ml[1] = l;
+    } else if (a.lse) {
+      a.lse[t * H + c] = n > 0 ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+  if (partial) {
+    float* op = a.part_o + ((t * a.splits + sp) * H + c) * (int64_t)D + 4 * g;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) *(v4f*)(op + 16 * d) = o[d];
+  } else {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = (uint16_t*)a.out + (t * H + c) * (int64_t)D + 4 * g;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      v2i pk;
+      pk[0] = (int)pack_bf16x2(o[d][0] * inv, o[d][1] * inv);
+      pk[1] = (int)pack_bf16x2(o[d][2] * inv, o[d][3] * inv);
+      *(v2i*)(op + 16 * d) = pk;
+    }
   }
 }
 
@@ -905,6 +1106,17 @@ static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStre
   return hipGetLastError();
 }
 
+template <bool SEPV>
+static hipError_t launch_h16(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
+  constexpr size_t lds = 2 * (size_t)(SEPV ? 8192 : 4096) + 3 * 16 * 4;
+  attn_h16_kernel<SEPV><<<(unsigned)(a.T * a.splits), 64, lds, st>>>(a, seq_off);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  const int64_t per_blk = 256 / (a.Dv / 4);
+  attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 static hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
   const int64_t per_blk = 256 / (a.Dv / 4);
   attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
@@ -940,8 +1152,8 @@ hipError_t launch_attn(const AttnArgs& a_in, bool f32, void* ws, size_t ws_bytes
     return hipGetLastError();
   }
   if (a.H == 16 && a.Dk == 128 && a.Dv == 128) {
-    if (a.v) return launch_bf16<128, 128, 1, true>(a, a.seq_offsets, st);
-    return launch_bf16<128, 128, 1, false>(a, a.seq_offsets, st);
+    if (a.v) return launch_h16<true>(a, a.seq_offsets, st);
+    return launch_h16<false>(a, a.seq_offsets, st);
   }
   if (a.H == 128 && a.Dk == 576 && a.Dv == 512) {
     if (a.v) return launch_bf16<576, 512, 8, true>(a, a.seq_offsets, st);
