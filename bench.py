@@ -826,8 +826,8 @@ def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, d
         pairs = int((idx >= 0).sum())
         flops = 2.0 * spec.H * (spec.Dk + spec.Dv) * pairs
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    kern = "attn_mla_kernel" if (spec.H, spec.Dk, spec.Dv) == (128, 576, 512) and x["v"] is None \
-        else "attn_bf16_kernel"
+    kern = ("attn_mla_kernel" if (spec.H, spec.Dk, spec.Dv) == (128, 576, 512) and x["v"] is None
+            else "attn_h16_kernel" if (spec.H, spec.Dk, spec.Dv) == (16, 128, 128) else "attn_bf16_kernel")
     sha = kernel_source_sha(["attn.hip", "common.h", "kernels.h"])
     traffic = load_traffic(kern, sha) if spec is not None and L == 131072 else None
     roof = {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -841,6 +841,12 @@ def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, d
                 "achieved": round(idx_tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(idx_tf / PEAK_FP8_TFLOPS, 4), "algorithmic_flops": ifl,
                 "note": "step minus attention, timed live; per-kernel times under 'kernels' (committed trace)"}
+    # the rows the attention gathers: one latent row per pair (shared K/V), else
+    # a key row and a value row; for few heads this, not the MFMA work, bounds it
+    row_bytes = 2 * (spec.Dk + (spec.Dv if x["v"] is not None else 0))
+    gathered = pairs * row_bytes
+    roof["gathered_bytes_per_launch"] = gathered
+    roof["gather_gbps"] = round(gathered / (attn_ms * 1e-3) / 1e9, 1)
     if peaks:
         roof["frac_measured_peak"] = round(achieved / peaks["bf16_tflops"], 4)
         roof_idx["frac_measured_peak"] = round(idx_tf / peaks["fp8_tflops"], 4)
