@@ -355,15 +355,18 @@ def run_decode(spec, x, dev):
 
 
 DEC_SMALL = gen.DECODE_64.with_(name="decode_B7_small", B=7, n_min=1, n_max=3000, topk=512)
+# 16 heads of 128 over shared key/value rows: the 16-head attention kernel
+# with per-sequence row bases and key splits
+DEC_H16 = DEC_SMALL.with_(name="decode_B7_h16", H=16, Dk=128, Dv=128)
 
 
-@pytest.mark.parametrize("spec", [DEC_SMALL, gen.DECODE_64], ids=["small", "B64_full"])
+@pytest.mark.parametrize("spec", [DEC_SMALL, DEC_H16, gen.DECODE_64], ids=["small", "h16", "B64_full"])
 def test_forward_decode(dev, spec):
     """Every sequence of the batch against the oracle: indices under the
     window rule, attention over the kept set."""
     say("forward decode", spec.name)
     lengths = None
-    if spec is DEC_SMALL:
+    if spec.B == 7:
         lengths = torch.tensor([1, 2, 511, 512, 513, 2999, 1000], dtype=torch.int64)
     x = gen.make_decode(spec, seed=10, device=dev, lengths=lengths)
     out, idx = run_decode(spec, x, dev)
