@@ -939,7 +939,9 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
 // merge the key splits of each (query, head): weights 2^(m_s - M) with M the
 // largest split max; out = sum_s w_s O_s / sum_s w_s l_s (bf16), lse in ln.
 // Dv/4 threads per (query, head), four value columns each.
+// NS >= splits slots (2, 4 or 8: the launcher rounds up).
 constexpr int kMaxSplits = 8;
+template <int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int tph = (int)(a.Dv / 4);
   const int per_blk = 256 / tph;
@@ -948,26 +950,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int d = 4 * (threadIdx.x % tph);
   const int64_t t = th / a.H, h = th % a.H;
   const int S = a.splits;
-  float ms[kMaxSplits], ls[kMaxSplits];
+  // every split block writes its (max, sum) and its partial (zeros and
+  // (-inf, 0) when it had no keys), so all loads go out at once, with no
+  // branch around them (slots past S re-read split S - 1 and are not used)
+  float2 ml[NS];
+  v4f po[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int ss = s < S ? s : S - 1;
+    ml[s] = *(const float2*)(a.part_ml + ((t * S + ss) * a.H + h) * 2);
+    po[s] = *(const v4f*)(a.part_o + ((t * S + ss) * a.H + h) * a.Dv + d);
+  }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < S) {
-      const float2 ml = *(const float2*)(a.part_ml + ((t * S + s) * a.H + h) * 2);
-      ms[s] = ml.x;
-      ls[s] = ml.y;
-      M = fmaxf(M, ml.x);
-    }
-  }
+  for (int s = 0; s < NS; ++s)
+    if (s < S) M = fmaxf(M, ml[s].x);
   float L = 0.f;
   v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < S && ls[s] > 0.f) {
-      const float wgt = exp2f(ms[s] - M);
-      L += ls[s] * wgt;
-      acc += wgt * *(const v4f*)(a.part_o + ((t * S + s) * a.H + h) * a.Dv + d);
-    }
+  for (int s = 0; s < NS; ++s) {
+    // weight 0 for unused slots and empty splits (their partials are finite)
+    const bool use = s < S && ml[s].y > 0.f;
+    const float wgt = use ? exp2f(ml[s].x - M) : 0.f;
+    L += use ? ml[s].y * wgt : 0.f;
+    acc += wgt * po[s];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   v2i pk;
@@ -975,6 +981,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   pk[1] = (int)pack_bf16x2(acc[2] * inv, acc[3] * inv);
   *(v2i*)((uint16_t*)a.out + (t * a.H + h) * a.Dv + d) = pk;
   if (a.lse && d == 0) a.lse[t * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+static void launch_combine_kernel(const AttnArgs& a, int64_t per_blk, hipStream_t st) {
+  const unsigned grid = (unsigned)((a.T * a.H + per_blk - 1) / per_blk);
+  if (a.splits <= 2)
+    attn_combine_kernel<2><<<grid, 256, 0, st>>>(a);
+  else if (a.splits <= 4)
+    attn_combine_kernel<4><<<grid, 256, 0, st>>>(a);
+  else
+    attn_combine_kernel<kMaxSplits><<<grid, 256, 0, st>>>(a);
 }
 
 // ---- fp32 path -----------------------------------------------------------
@@ -1102,7 +1118,7 @@ static hipError_t launch_bf16(const AttnArgs& a, const int64_t* seq_off, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   const int64_t per_blk = 256 / (a.Dv / 4);
-  attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
+  launch_combine_kernel(a, per_blk, st);
   return hipGetLastError();
 }
 
@@ -1113,13 +1129,13 @@ static hipError_t launch_h16(const AttnArgs& a, const int64_t* seq_off, hipStrea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   const int64_t per_blk = 256 / (a.Dv / 4);
-  attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
+  launch_combine_kernel(a, per_blk, st);
   return hipGetLastError();
 }
 
 static hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
   const int64_t per_blk = 256 / (a.Dv / 4);
-  attn_combine_kernel<<<(unsigned)((a.T * a.H + per_blk - 1) / per_blk), 256, 0, st>>>(a);
+  launch_combine_kernel(a, per_blk, st);
   return hipGetLastError();
 }
 
