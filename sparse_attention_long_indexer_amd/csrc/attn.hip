@@ -141,6 +141,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   constexpr int TILE_BYTES = TILE_CHUNKS * 16;
   static_assert(KC % 4 == 0 && VC % 4 == 0, "fragments are 4 chunks wide");
   static_assert(DV % (16 * NW) == 0, "value columns split evenly over the waves");
+  static_assert(DV / NW == 64, "each wave reads its four value subtiles in one asm block");
   constexpr int KF = 2 * (KC / 4);              // K fragments per tile
   constexpr int NFRAG = KF + 2 * (VC / 4);      // fragments per tile
   constexpr int LOADS = (NFRAG + NW - 1) / NW;  // fragment copies per wave per tile
@@ -326,20 +327,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
     // O^T += V^T . P^T over this wave's value columns
     {
       const char* vb = SEPV ? tb + KF * 1024 : tb;
+      // subtiles D = 4w .. 4w+3 sit in fragments 2w, 2w+1 of each key subtile
       v8s av[ND];
-      if constexpr (ND == 4) {
-        // subtiles D = 4w .. 4w+3 sit in fragments 2w, 2w+1 of each key subtile
-        lds_read_vt4<VF * 1024>(vb + vbase + 2048 * w, av);
-      } else {
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int D = ND * w + d;                 // value subtile index
-          const int off = vbase + ((D >> 1) * 4 + 2 * (D & 1)) * 256;
-          const v4s lo = lds_read_tr16(vb, off);
-          const v4s hi = lds_read_tr16(vb, off + VF * 1024);
-          av[d] = (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      }
+      lds_read_vt4<VF * 1024>(vb + vbase + 2048 * w, av);
 #pragma unroll
       for (int hs = 0; hs < NW; ++hs) {
         const v8s pf = *(const v8s*)(pbuf + (hs * 64 + lane) * 16);
