@@ -344,7 +344,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
 
   // epilogue: row sums of every head, then lane (c, g) of wave w writes
   // O^T[dv = DVW*w + 16d + 4g + i][head 16hs + c]: normalised bf16 output,
-  // or with several splits the unnormalised fp32 partial plus (max, sum)
+  // or with several splits the unnormalised partial as fp16 over its
+  // 64-column slice scale, plus (max, sum)
   const bool partial = a.splits > 1;
   {
     const float l = rows_sum(l_part);
@@ -365,9 +366,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
   for (int hs = 0; hs < NW; ++hs) {
     const int h = 16 * hs + c;
     if (partial) {
-      float* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + DVW * w;
+      // slice w of head h: the lane's 16 values, then the four lanes of the head
+      float mx = 0.f;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) *(v4f*)(op + 16 * d + 4 * g) = o[d][hs];
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(o[d][hs][i]));
+      mx = rows_max(mx);
+      const float sc = mx > 0.f ? mx : 1.f, isc = 1.f / sc;
+      if (g == 0) a.part_sc[((t * a.splits + sp) * H + h) * (DV / 64) + w] = sc;
+      uint16_t* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + DVW * w;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const v2i pk = {(int)pack_f16x2(o[d][hs][0] * isc, o[d][hs][1] * isc),
+                        (int)pack_f16x2(o[d][hs][2] * isc, o[d][hs][3] * isc)};
+        *(v2i*)(op + 16 * d + 4 * g) = pk;
+      }
     } else {
       const float l = s_l[h];
       const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -579,7 +593,8 @@ __global__ __launch_bounds__(64) void attn_h16_kernel(AttnArgs a, const int64_t*
 
   // epilogue: row sums per head, then lane (c, g) writes O^T[dv = 16d + 4g
   // + i][head c]: normalised bf16 output, or with several splits the
-  // unnormalised fp32 partial plus (max, sum)
+  // unnormalised partial as fp16 over its 64-column slice scales, plus
+  // (max, sum)
   const bool partial = a.splits > 1;
   const float l = rows_sum(l_part);
   if (g == 0) {
@@ -592,9 +607,24 @@ __global__ __launch_bounds__(64) void attn_h16_kernel(AttnArgs a, const int64_t*
     }
   }
   if (partial) {
-    float* op = a.part_o + ((t * a.splits + sp) * H + c) * (int64_t)D + 4 * g;
+    uint16_t* op = a.part_o + ((t * a.splits + sp) * H + c) * (int64_t)D + 4 * g;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) *(v4f*)(op + 16 * d) = o[d];
+    for (int q = 0; q < D / 64; ++q) {
+      // slice q = subtiles 4q .. 4q+3: the lane's 16 values, then the head's four lanes
+      float mx = 0.f;
+#pragma unroll
+      for (int d = 4 * q; d < 4 * q + 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(o[d][i]));
+      mx = rows_max(mx);
+      const float sc = mx > 0.f ? mx : 1.f, isc = 1.f / sc;
+      if (g == 0) a.part_sc[((t * a.splits + sp) * H + c) * (D / 64) + q] = sc;
+#pragma unroll
+      for (int d = 4 * q; d < 4 * q + 4; ++d) {
+        const v2i pk = {(int)pack_f16x2(o[d][0] * isc, o[d][1] * isc), (int)pack_f16x2(o[d][2] * isc, o[d][3] * isc)};
+        *(v2i*)(op + 16 * d) = pk;
+      }
+    }
   } else {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* op = (uint16_t*)a.out + (t * H + c) * (int64_t)D + 4 * g;
@@ -879,16 +909,32 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
   }
   __syncthreads();
   if (partial) {
+    // the unnormalised partial as fp16 over a scale per (head, 64-column
+    // slice w): lanes l and l ^ 32 hold the slice's 64 values of head h
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
       const int h = 32 * hb + (lane & 31);
-      float* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + 64 * w + 4 * (lane >> 5);
+      float mx = 0.f;
 #pragma unroll
       for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          *(v4f*)(op + 32 * vb + 8 * rq) =
-              (v4f){o[vb][hb][4 * rq], o[vb][hb][4 * rq + 1], o[vb][hb][4 * rq + 2], o[vb][hb][4 * rq + 3]};
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(o[vb][hb][r]));
+      {
+        const uint32_t u = __float_as_uint(mx);
+        auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float sc = mx > 0.f ? mx : 1.f, isc = 1.f / sc;
+      if (lane < 32) a.part_sc[((t * a.splits + sp) * H + h) * (DV / 64) + w] = sc;
+      uint16_t* op = a.part_o + ((t * a.splits + sp) * H + h) * (int64_t)DV + 64 * w + 4 * (lane >> 5);
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const v2i pk = {(int)pack_f16x2(o[vb][hb][4 * rq] * isc, o[vb][hb][4 * rq + 1] * isc),
+                          (int)pack_f16x2(o[vb][hb][4 * rq + 2] * isc, o[vb][hb][4 * rq + 3] * isc)};
+          *(v2i*)(op + 32 * vb + 8 * rq) = pk;
+        }
     }
     return;
   }
@@ -927,8 +973,9 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
 }
 
 // merge the key splits of each (query, head): weights 2^(m_s - M) with M the
-// largest split max; out = sum_s w_s O_s / sum_s w_s l_s (bf16), lse in ln.
-// Dv/4 threads per (query, head), four value columns each.
+// largest split max; out = sum_s w_s O_s / sum_s w_s l_s (bf16), lse in ln,
+// where O_s is the fp16 partial times its 64-column slice scale.  Dv/4
+// threads per (query, head), four value columns each.
 // NS >= splits slots (2, 4 or 8: the launcher rounds up).
 constexpr int kMaxSplits = 8;
 template <int NS>
@@ -943,13 +990,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   // every split block writes its (max, sum) and its partial (zeros and
   // (-inf, 0) when it had no keys), so all loads go out at once, with no
   // branch around them (slots past S re-read split S - 1 and are not used)
+  const int nsl = (int)(a.Dv / 64);
   float2 ml[NS];
-  v4f po[NS];
+  float sc[NS];
+  v2i po[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int ss = s < S ? s : S - 1;
-    ml[s] = *(const float2*)(a.part_ml + ((t * S + ss) * a.H + h) * 2);
-    po[s] = *(const v4f*)(a.part_o + ((t * S + ss) * a.H + h) * a.Dv + d);
+    const int64_t th_s = (t * S + ss) * a.H + h;
+    ml[s] = *(const float2*)(a.part_ml + th_s * 2);
+    sc[s] = a.part_sc[th_s * nsl + (d >> 6)];
+    po[s] = *(const v2i*)(a.part_o + th_s * a.Dv + d);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -963,7 +1014,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const bool use = s < S && ml[s].y > 0.f;
     const float wgt = use ? exp2f(ml[s].x - M) : 0.f;
     L += use ? ml[s].y * wgt : 0.f;
-    acc += wgt * po[s];
+    acc += (wgt * sc[s]) * unpack_f16x4(po[s]);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   v2i pk;
@@ -1092,8 +1143,8 @@ static int attn_splits(bool f32, int64_t T, int64_t k) {
 size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t k) {
   const int s = attn_splits(f32, T, k);
   if (s <= 1) return 0;
-  const size_t o = (size_t)T * s * H * Dv * 4, ml = (size_t)T * s * H * 2 * 4;
-  return (o + 255) / 256 * 256 + ml;
+  const size_t o = (size_t)T * s * H * Dv * 2, ml = (size_t)T * s * H * 2 * 4, sc = (size_t)T * s * H * (Dv / 64) * 4;
+  return (o + 255) / 256 * 256 + (ml + 255) / 256 * 256 + sc;
 }
 
 template <int DK, int DV, int NW, bool SEPV>
@@ -1148,9 +1199,11 @@ hipError_t launch_attn(const AttnArgs& a_in, bool f32, void* ws, size_t ws_bytes
   a.splits = attn_splits(f32, a.T, a.k);
   if (a.splits > 1) {
     if (!ws || ws_bytes < attn_workspace_bytes(f32, a.T, a.H, a.Dv, a.k)) return hipErrorInvalidValue;
-    a.part_o = (float*)ws;
-    a.part_ml = (float*)((char*)ws + ((size_t)a.T * a.splits * a.H * a.Dv * 4 + 255) / 256 * 256);
-    DSA_DEBUG_CHECK((char*)(a.part_ml + (size_t)a.T * a.splits * a.H * 2) <= (char*)ws + ws_bytes);
+    const size_t rows = (size_t)a.T * a.splits * a.H;
+    a.part_o = (uint16_t*)ws;
+    a.part_ml = (float*)((char*)ws + (rows * a.Dv * 2 + 255) / 256 * 256);
+    a.part_sc = (float*)((char*)a.part_ml + (rows * 2 * 4 + 255) / 256 * 256);
+    DSA_DEBUG_CHECK((char*)(a.part_sc + rows * (a.Dv / 64)) <= (char*)ws + ws_bytes);
   }
   if (f32) {
     a.splits = 1;

@@ -92,6 +92,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
 }
 
+// two floats -> packed fp16 pair (round to nearest even), and four packed
+// fp16 values back to floats
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2f x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2h));
+}
+__device__ __forceinline__ v4f unpack_f16x4(v2i p) {
+  typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+  return __builtin_convertvector(__builtin_bit_cast(v4h, p), v4f);
+}
+
 // Order-preserving map of a float score to uint32 (larger score -> larger
 // key); -0.0 is folded onto +0.0 so that zeros tie.
 __device__ __forceinline__ uint32_t score_key(float f) {

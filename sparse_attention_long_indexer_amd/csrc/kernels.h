@@ -127,8 +127,9 @@ struct AttnArgs {
   void* out;            // [T][H][Dv]
   float* lse;           // [T][H] or nullptr
   int splits;           // key splits per query (set by launch_attn)
-  float* part_o;        // [T][splits][H][Dv] unnormalised partial outputs
+  uint16_t* part_o;     // [T][splits][H][Dv] fp16: unnormalised partial output / its slice scale
   float* part_ml;       // [T][splits][H][2] running max (log2) and sum
+  float* part_sc;       // [T][splits][H][Dv/64] slice scales: max |partial| over 64 value columns
 };
 bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int64_t k);
 size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t k);
