@@ -45,7 +45,10 @@ __device__ __forceinline__ uint32_t block_prefix(bool pred, uint32_t* wave_cnt, 
 // per-lane atomics, which keeps heavy ties (ReLU zeros) cheap.
 // Returns thr (the m-th largest key) and need (how many keys equal to thr
 // belong to the top m).  hist must hold 1024 words; scan holds NT/64 words.
-template <int NT, class KeyAt>
+// With MAXPASS < 4 the digits below the last pass are left at zero: thr is
+// then a lower bound of the m-th largest key within 2^(top - 10 MAXPASS + 1)
+// of it (top = the span's highest bit), and need is not meaningful.
+template <int NT, class KeyAt, int MAXPASS = 4>
 __device__ inline void radix_select(KeyAt key_at, int64_t n, uint32_t m, uint32_t lo, uint32_t hi,
                                     uint32_t* hist, uint32_t* scan, uint32_t* s_out, uint32_t& thr,
                                     uint32_t& need) {
@@ -54,7 +57,7 @@ __device__ inline void radix_select(KeyAt key_at, int64_t n, uint32_t m, uint32_
   const uint32_t span = hi - lo;
   int top = span ? 31 - __builtin_clz(span) : 0;      // highest set bit of the span
   uint32_t prefix = 0, pmask = 0, remaining = m;
-  for (int shift = top - 9; ; shift -= 10) {
+  for (int shift = top - 9, pass = 1; ; shift -= 10, ++pass) {
     const int sh = shift > 0 ? shift : 0;
     const uint32_t dmask = shift >= 0 ? 1023u : (1023u >> (-shift));
     for (int i = tid; i < BINS; i += NT) hist[i] = 0;
@@ -113,7 +116,7 @@ __device__ inline void radix_select(KeyAt key_at, int64_t n, uint32_t m, uint32_
     prefix |= dig << sh;
     pmask |= dmask << sh;
     __syncthreads();
-    if (shift <= 0) break;
+    if (shift <= 0 || pass >= MAXPASS) break;
   }
   thr = lo + prefix;
   need = remaining;

@@ -168,12 +168,15 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_estimate_kernel(TopkRo
     mx = max(mx, hist[kCandWaves + i]);
   }
   __syncthreads();
+  // the threshold only sets how many candidates the filter keeps, so two
+  // digit passes (within 2^(top - 19) of the exact r-th sample) suffice
   uint32_t thr, need;
+  auto staged_at = [&](int64_t i) { return skey[i]; };
   if (staged)
-    radix_select<kCandThreads>([&](int64_t i) { return skey[i]; }, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr,
-                               need);
+    radix_select<kCandThreads, decltype(staged_at), 2>(staged_at, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr,
+                                                       need);
   else
-    radix_select<kCandThreads>(key_at, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr, need);
+    radix_select<kCandThreads, decltype(key_at), 2>(key_at, nsamp, (uint32_t)r, mn, mx, hist, scan, s_out, thr, need);
   if (tid == 0) tau[row] = thr == kZeroKey ? kZeroKey + 1 : thr;
 }
 
