@@ -16,8 +16,9 @@ The dominant kernel's duration is measured live with HIP events on the stream
 the kernel runs on; its roofline uses algorithmic FLOPs (or bytes) only, and
 is stated against both the published peak and the peak measured in the same
 run by the probe library (an MFMA issue loop and a streaming HBM read).  GPU
-clocks and power are read before, during (sampled while the timed steps
-run) and after the timed region.  The 8K and 32K prefills are timed as extra
+clocks and power are read before the timed region, during (sampled while
+about 4 s of further, untimed steps of the same workload run right after
+it) and after.  The 8K and 32K prefills are timed as extra
 lines; decode is timed warm (one cache set) and
 cold (four cache sets in rotation, 24 GB, far past the 256 MB last-level
 cache).  The CPU baseline times the fp64 oracle on a stratified sample of
@@ -158,7 +159,8 @@ def clock_summary(flat):
 
 class ClockSampler:
     """Reads the clocks once on a helper thread while the GPU runs queued
-    work (the host is blocked in a synchronisation meanwhile)."""
+    work (the host is blocked in a synchronisation meanwhile; the caller
+    queues enough work to outlast the tool's start-up)."""
 
     def __init__(self):
         import threading
@@ -795,10 +797,17 @@ def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, d
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
-    sampler = ClockSampler().start() if keep else None   # while the queued steps run
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
-    clocks_during = sampler.join() if sampler else None
+    clocks_during = None
+    if keep:
+        # the clock tool takes about a second to start: read it while further
+        # untimed steps of the same workload keep the GPU busy for ~4 s
+        for _ in range(max(1, int(math.ceil(4.0 / dt)))):
+            step()
+        sampler = ClockSampler().start()
+        torch.cuda.synchronize()
+        clocks_during = sampler.join()
     log(f"{spec.name}: prefill {dt * 1e3:.2f} ms/step, {L / dt:.4g} tokens/s")
     del ws
 
