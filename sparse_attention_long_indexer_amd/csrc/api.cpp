@@ -456,7 +456,7 @@ dsa_status_t forward_run(const dsa_forward_args* a, int32_t* idx_out, void* out,
     at.S = S;
   } else {
     e = launch_index_scores_decode((const uint8_t*)qf, qs, (const uint8_t*)a->k_idx, a->k_scale,
-                                   a->seq_offsets, R, a->max_len, sc, st);
+                                   a->seq_offsets, R, a->total_keys, sc, st);
     if (e != hipSuccess) return DSA_ERR_DEVICE;
     TopkRows tr{sc, 0, nullptr, nullptr, 0, a->seq_offsets, 0, 0};
     e = launch_topk(tr, R, a->max_len, a->topk, idx, nullptr, p.topk_bytes ? base + p.topk_off : nullptr, st,

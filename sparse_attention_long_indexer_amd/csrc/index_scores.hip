@@ -121,15 +121,22 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
 // ---- decode: one query per sequence against its own cache ----------------
 //
 // Bound by the HBM read of the cached index keys (132 bytes per key with its
-// scale).  Block (x, b) covers 256 keys of sequence b, 64 per wave.  A wave
-// copies its 64 keys (8 KB, contiguous in the cache) straight into its own
-// LDS region with eight 1 KB direct-to-LDS copies, each covering 8 whole key
-// rows (8 lanes per 128-byte row), issued non-temporal since every cached
-// key is read once per step; then reads them back in the MFMA's operand
-// layout.  Within a row the 16-byte chunk j of key r sits in slot
-// j ^ ((r >> 1) & 7), so that the 16 lanes reading one chunk of 16
-// consecutive keys hit 16 distinct bank groups.  The query row is
-// replicated over the 16 A rows so every C row holds the same 16 scores.
+// scale).  The grid covers the concatenated caches of all sequences: block
+// x covers flat keys 256 x .. +255, 64 per wave, so no block is spent on the
+// gap between a short sequence and the longest one.  A wave copies its 64
+// keys (8 KB, contiguous) straight into its own LDS region with eight 1 KB
+// direct-to-LDS copies, each covering 8 whole key rows (8 lanes per 128-byte
+// row), issued non-temporal since every cached key is read once per step;
+// then reads them back in the MFMA's operand layout.  Within a row the
+// 16-byte chunk j of key r sits in slot j ^ ((r >> 1) & 7), so that the 16
+// lanes reading one chunk of 16 consecutive keys hit 16 distinct bank
+// groups.  While the copies fly, the wave finds the sequence b0 of its first
+// key (a ballot over 64 sequence ends at a time).  A wave inside one
+// sequence replicates that query over the 16 A rows; a wave that straddles
+// sequence ends gives A row c of each 16-key group the query of sequence
+// (the group's first key's) + c, and each key takes the C row of its own
+// sequence (every score is the same per-element MFMA dot product either
+// way, so the scores match the prefill scores kernel bit for bit).
 #ifndef DSA_DEC_WAVE_KEYS
 #define DSA_DEC_WAVE_KEYS 64
 #endif
@@ -139,28 +146,29 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
 constexpr int kDecWaveKeys = DSA_DEC_WAVE_KEYS;
 constexpr int kDecKeysPerBlock = 4 * kDecWaveKeys;
 constexpr int kNtAux = DSA_DEC_NT;   // cache-policy operand of the copies: 2 = non-temporal
+static_assert(kDecWaveKeys == 64, "a straddling wave looks up one sequence end per lane");
 
 __global__ __launch_bounds__(256) void index_scores_decode_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k,
-    const float* __restrict__ ks, const int64_t* __restrict__ off, int64_t b0, float* __restrict__ out) {
+    const float* __restrict__ ks, const int64_t* __restrict__ off, int64_t B, int64_t total,
+    float* __restrict__ out) {
   constexpr int J = kDecWaveKeys / 16;   // 16-key MFMA groups per wave
   constexpr int NI = kDecWaveKeys / 8;   // 1 KB copies per wave
   __shared__ __align__(16) uint8_t kbuf[4][kDecWaveKeys * kIdxDim];
+  __shared__ int64_t send[4][kDecWaveKeys + 1];   // a straddling wave's sequence ends
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t b = b0 + blockIdx.y;
-  const int64_t lo = off[b], n = off[b + 1] - lo;
-  const int64_t sw = (int64_t)blockIdx.x * kDecKeysPerBlock + w * kDecWaveKeys;
-  if (sw >= n) return;
+  const int64_t k0 = (int64_t)blockIdx.x * kDecKeysPerBlock + w * kDecWaveKeys;   // flat
+  if (k0 >= total) return;
   // copy i: lane l brings chunk (l % 8) ^ f(r) of key r = 8 i + l / 8 (keys
-  // past the sequence's end read its last key; their scores are dropped)
+  // past the last cached key read it again; their scores are dropped)
   {
     const int rl = lane >> 3;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = 8 * i + rl;
-      const int64_t s = sw + r;
-      const int64_t sb = lo + (s < n ? s : n - 1);
+      const int64_t s = k0 + r;
+      const int64_t sb = s < total ? s : total - 1;
       const int j = (lane & 7) ^ ((r >> 1) & 7);
       __builtin_amdgcn_global_load_lds(
           (const void*)(k + sb * kIdxDim + 16 * j),
@@ -171,43 +179,92 @@ __global__ __launch_bounds__(256) void index_scores_decode_kernel(
   float kss[J];
 #pragma unroll
   for (int jj = 0; jj < J; ++jj) {
-    const int64_t s = sw + 16 * jj + c;
-    kss[jj] = __builtin_nontemporal_load(ks + lo + (s < n ? s : n - 1));
+    const int64_t s = k0 + 16 * jj + c;
+    kss[jj] = __builtin_nontemporal_load(ks + (s < total ? s : total - 1));
   }
-  const v8i a = *(const v8i*)(qf + b * kIdxDim + 32 * g);
-  const float qsc = qs[b];
+  // b0 = the sequence of key k0 = how many sequence ends off[1..B] are <= k0
+  // (off[B] = total > k0, so the search ends in the round holding it)
+  int64_t b0 = 0, e0 = total;
+  for (int64_t base = 1; base <= B; base += 64) {
+    const int64_t i = base + lane;
+    const int64_t ov = i <= B ? off[i] : (int64_t)0x7FFFFFFFFFFFFFFFLL;
+    const uint64_t le = ballot(ov <= k0);
+    const int cnt = __popcll(le);
+    b0 += cnt;
+    if (cnt < 64) {
+      const int lo32 = __shfl((int)(uint32_t)ov, cnt), hi32 = __shfl((int)(ov >> 32), cnt);
+      e0 = (int64_t)(((uint64_t)(uint32_t)hi32 << 32) | (uint32_t)lo32);   // end of sequence b0
+      break;
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed (its own LDS region)
-#pragma unroll
-  for (int jj = 0; jj < J; ++jj) {
+  auto keys_of = [&](int jj) {
     const int r = 16 * jj + c;
     const uint8_t* row = kbuf[w] + 1024 * (r >> 3) + 128 * (r & 7);
     const int f = (r >> 1) & 7;
     const v4i h0 = *(const v4i*)(row + 16 * ((2 * g) ^ f));
     const v4i h1 = *(const v4i*)(row + 16 * ((2 * g + 1) ^ f));
-    const v8i bb = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-    const int64_t s = sw + r;
+    return (v8i){h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  };
+  if (e0 >= k0 + kDecWaveKeys) {
+    // the whole wave lies in sequence b0
+    const v8i a = *(const v8i*)(qf + b0 * kIdxDim + 32 * g);
+    const float qsc = qs[b0];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) {
+      const int64_t s = k0 + 16 * jj + c;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_fp8_16x16x128(a, keys_of(jj), acc);
+      if (g == 0 && s < total) {
+        const float u = acc[0] * kss[jj] * qsc;
+        out[s] = u > 0.f ? u : 0.f;
+      }
+    }
+    return;
+  }
+  // straddling wave: ends of sequences b0 .. b0 + 64 (at most 64 sequences
+  // own its 64 keys), then per key its sequence by binary search
+  int64_t* se = send[w];
+  se[lane] = off[b0 + lane <= B ? b0 + lane : B];
+  if (lane == 0) se[64] = off[b0 + 64 <= B ? b0 + 64 : B];
+  __builtin_amdgcn_wave_barrier();
+  auto seq_of = [&](int64_t p) {   // largest j with se[j] <= p, for se[0] <= p < se[64]
+    int lo = 0, hi = 64;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (se[mid] <= p) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    const int64_t s = k0 + 16 * jj + c;
+    const int64_t sv = s < total ? s : total - 1;
+    const int sq = seq_of(sv);                       // key's sequence - b0
+    const int sa = __shfl(sq, 16 * g);               // the group's first key's (lane c = 0)
+    const int64_t qa = b0 + sa + c < B ? b0 + sa + c : B - 1;
+    const v8i a = *(const v8i*)(qf + qa * kIdxDim + 32 * g);
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma_fp8_16x16x128(a, bb, acc);
-    if (g == 0 && s < n) {
-      const float u = acc[0] * kss[jj] * qsc;
-      out[lo + s] = u > 0.f ? u : 0.f;
+    acc = mfma_fp8_16x16x128(a, keys_of(jj), acc);
+    const int d = sq - sa;                           // 0 .. 15: the key's C row
+    if (s < total && (d >> 2) == g) {
+      const int q = d & 3;
+      const float v = q == 0 ? acc[0] : q == 1 ? acc[1] : q == 2 ? acc[2] : acc[3];
+      const float u = v * kss[jj] * qs[b0 + sq];
+      out[s] = u > 0.f ? u : 0.f;
     }
   }
 }
 
 hipError_t launch_index_scores_decode(const uint8_t* qf, const float* qs, const uint8_t* k,
                                       const float* ks, const int64_t* offsets, int64_t B,
-                                      int64_t max_len, float* out, hipStream_t st) {
-  if (B <= 0 || max_len <= 0) return hipSuccess;
-  // sequences run along the grid's y extent (at most 65535 per launch)
-  for (int64_t b0 = 0; b0 < B; b0 += kMaxGridY) {
-    const int64_t nb = B - b0 < kMaxGridY ? B - b0 : kMaxGridY;
-    dim3 grid((unsigned)((max_len + kDecKeysPerBlock - 1) / kDecKeysPerBlock), (unsigned)nb);
-    index_scores_decode_kernel<<<grid, 256, 0, st>>>(qf, qs, k, ks, offsets, b0, out);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+                                      int64_t total_keys, float* out, hipStream_t st) {
+  if (B <= 0 || total_keys <= 0) return hipSuccess;
+  const int64_t blocks = (total_keys + kDecKeysPerBlock - 1) / kDecKeysPerBlock;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  index_scores_decode_kernel<<<(unsigned)blocks, 256, 0, st>>>(qf, qs, k, ks, offsets, B, total_keys, out);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -37,9 +37,10 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
                                int64_t row_begin, int64_t row_end, float* out, int64_t ld,
                                hipStream_t st);
 // decode: scores of query b over its own cache rows, written at key offsets
+// (total_keys = offsets[B], the concatenated caches' length)
 hipError_t launch_index_scores_decode(const uint8_t* qf, const float* qs, const uint8_t* k,
                                       const float* ks, const int64_t* offsets, int64_t B,
-                                      int64_t max_len, float* out, hipStream_t st);
+                                      int64_t total_keys, float* out, hipStream_t st);
 
 // Dynamic k (every selection path): a row keeps
 // min(n, k, max(k_min, #{scores > theta})) keys; theta = -inf keeps the
