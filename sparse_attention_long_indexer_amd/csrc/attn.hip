@@ -31,10 +31,8 @@
 
 namespace dsa {
 
-#ifndef DSA_QK_GROUP
-#define DSA_QK_GROUP 4  // QK k-steps the scheduler may interleave
-#define DSA_PV_GROUP 4  // PV dv-subtiles the scheduler may interleave
-#endif
+constexpr int kQkGroup = 4;  // QK k-steps the scheduler may interleave
+constexpr int kPvGroup = 4;  // PV head subtiles the scheduler may interleave
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -278,7 +276,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
         const v8s kf = *(const v8s*)(tb + ((ks * (KC / 4) + kk) * 64 + kslot) * 16);
         sc[ks] = mfma_bf16_16x16x32(kf, qf[kk], sc[ks]);
       }
-      if (kk % DSA_QK_GROUP == DSA_QK_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+      if (kk % kQkGroup == kQkGroup - 1) __builtin_amdgcn_sched_barrier(0);
     }
     // online softmax (log2 domain); the running max only moves when a tile
     // raises it by more than 2^8, so O is rescaled rarely
@@ -335,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnArgs a, const
         const v8s pf = *(const v8s*)(pbuf + (hs * 64 + lane) * 16);
 #pragma unroll
         for (int d = 0; d < ND; ++d) o[d][hs] = mfma_bf16_16x16x32(av[d], pf, o[d][hs]);
-        if (hs % DSA_PV_GROUP == DSA_PV_GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+        if (hs % kPvGroup == kPvGroup - 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -665,9 +663,7 @@ __global__ __launch_bounds__(64) void attn_h16_kernel(AttnArgs a, const int64_t*
 constexpr int kMlaTile = 32 * (576 / 8) * 16;         // 32 latent rows, 36 KB
 constexpr size_t kMlaFixedLds = 3 * kMlaTile + 2 * 8 * 1024;
 
-#ifndef DSA_MLA_QKG
-#define DSA_MLA_QKG 2  // k-steps of S^T read per LDS round trip (2 fragments each)
-#endif
+constexpr int kMlaQkg = 2;  // k-steps of S^T reads in flight ahead of the MFMAs (2 fragments each)
 
 // 2^x with the hardware instruction alone: results below 2^-126 flush to
 // zero, which for softmax weights relative to a running max (sum >= 1) is
@@ -775,7 +771,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
     // issued before the MFMAs of k-step kk, so D steps of reads are in
     // flight behind the matrix core (the same registers as D reads per
     // round trip)
-    constexpr int D = DSA_MLA_QKG;
+    constexpr int D = kMlaQkg;
     v8s k0[KK], k1[KK];
 #pragma unroll
     for (int kk = 0; kk < D; ++kk) {

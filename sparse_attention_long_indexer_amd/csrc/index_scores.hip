@@ -137,16 +137,9 @@ hipError_t launch_index_scores(const void* qf, const float* qs, const void* k, c
 // (the group's first key's) + c, and each key takes the C row of its own
 // sequence (every score is the same per-element MFMA dot product either
 // way, so the scores match the prefill scores kernel bit for bit).
-#ifndef DSA_DEC_WAVE_KEYS
-#define DSA_DEC_WAVE_KEYS 64
-#endif
-#ifndef DSA_DEC_NT
-#define DSA_DEC_NT 2
-#endif
-constexpr int kDecWaveKeys = DSA_DEC_WAVE_KEYS;
+constexpr int kDecWaveKeys = 64;     // keys per wave (a straddling wave looks up one sequence end per lane)
 constexpr int kDecKeysPerBlock = 4 * kDecWaveKeys;
-constexpr int kNtAux = DSA_DEC_NT;   // cache-policy operand of the copies: 2 = non-temporal
-static_assert(kDecWaveKeys == 64, "a straddling wave looks up one sequence end per lane");
+constexpr int kNtAux = 2;            // cache-policy operand of the copies: 2 = non-temporal
 
 __global__ __launch_bounds__(256) void index_scores_decode_kernel(
     const uint8_t* __restrict__ qf, const float* __restrict__ qs, const uint8_t* __restrict__ k,
