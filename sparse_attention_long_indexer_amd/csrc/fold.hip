@@ -157,26 +157,30 @@ __global__ __launch_bounds__(512) void fold_split_kernel(const void* __restrict_
   }
 }
 
-// Long prefills (FP8 input, bf16 W): tiles of 64 rows, 256 threads, each
-// thread a register tile of 8 rows x 4 columns (32 fp64 accumulators), the
-// rows' dequantised values as fp64 in LDS (k-major, so a thread's 8 rows are
-// one 64-byte read) and W as fp32 in LDS (4 columns in one 16-byte read):
-// per k, 5 LDS reads and 4 conversions feed 32 fp64 FMAs.  A block converts
-// W once and walks tiles blockIdx.x, blockIdx.x + gridDim.x, ..., loading
-// the next tile's codes (32 bytes per thread) while it computes the current
-// one.  The per-row amax is a reduction over the 32 threads sharing the row.
-constexpr int kTileRows = 64;
+// Long prefills (FP8 input, bf16 W): tiles of TR rows (64, or 32 when 64-row
+// tiles would leave CUs idle), 256 threads, each thread a register tile of
+// TR/8 rows x 4 columns of fp64 accumulators, the rows' dequantised values as
+// fp64 in LDS (k-major, so a thread's rows are one contiguous read) and W as
+// fp32 in LDS (4 columns in one 16-byte read).  A block converts W once and
+// walks tiles blockIdx.x, blockIdx.x + gridDim.x, ..., loading the next
+// tile's codes while it computes the current one.  The per-row amax is a
+// reduction over the 32 threads sharing the row.
+template <int TR>
 __global__ __launch_bounds__(256, 1) void fold_tile_kernel(const uint8_t* __restrict__ q_in,
                                                            const float* __restrict__ q_scale,
                                                            const uint16_t* __restrict__ w_in, int64_t T,
                                                            uint8_t* __restrict__ q_out, float* __restrict__ s_out) {
+  constexpr int RPT = TR / 8;          // rows per thread
+  constexpr int TPR = 256 / TR;        // threads loading one row's codes
+  constexpr int CB = kIdxDim / TPR;    // code bytes per thread (32 or 16)
+  static_assert(TR == 32 || TR == 64, "tile heights of 32 or 64 rows");
   extern __shared__ __align__(16) char fold_smem[];
   float* sw = (float*)fold_smem;                                    // [k][j], 64 KB
-  double* sq = (double*)(fold_smem + kIdxDim * kIdxDim * 4);        // [k][row], 64 KB
+  double* sq = (double*)(fold_smem + kIdxDim * kIdxDim * 4);        // [k][row], 8 TR KB
   const int tid = threadIdx.x;
-  const int tx = tid & 31, ty = tid >> 5;   // columns 4 tx .. +3, rows 8 ty .. +7
-  const int lr = tid >> 2, lk = 32 * (tid & 3);  // the codes this thread loads: row lr, dims lk .. lk+31
-  const int64_t ntile = (T + kTileRows - 1) / kTileRows;
+  const int tx = tid & 31, ty = tid >> 5;   // columns 4 tx .. +3, rows RPT ty .. +RPT-1
+  const int lr = tid / TPR, lk = CB * (tid % TPR);  // the codes this thread loads: row lr, dims lk .. lk+CB-1
+  const int64_t ntile = (T + TR - 1) / TR;
   {
     uint4 wb[8];
 #pragma unroll
@@ -190,43 +194,46 @@ __global__ __launch_bounds__(256, 1) void fold_tile_kernel(const uint8_t* __rest
         *(float2*)(sw + e + 2 * h) = make_float2(__uint_as_float(u[h] << 16), __uint_as_float(u[h] & 0xFFFF0000u));
     }
   }
-  auto load = [&](int64_t tile, v8i& codes, float& scale) {
-    const int64_t t = tile * kTileRows + lr;
+  auto load = [&](int64_t tile, uint4 (&codes)[CB / 16], float& scale) {
+    const int64_t t = tile * TR + lr;
+#pragma unroll
+    for (int i = 0; i < CB / 16; ++i) codes[i] = make_uint4(0u, 0u, 0u, 0u);
+    scale = 0.f;
     if (tile < ntile && t < T) {
-      codes = *(const v8i*)(q_in + t * kIdxDim + lk);
+#pragma unroll
+      for (int i = 0; i < CB / 16; ++i) codes[i] = *(const uint4*)(q_in + t * kIdxDim + lk + 16 * i);
       scale = q_scale[t];
-    } else {
-      codes = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-      scale = 0.f;
     }
   };
-  v8i codes;
+  uint4 codes[CB / 16];
   float scale;
   load(blockIdx.x, codes, scale);
   for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
     __syncthreads();   // the previous tile's reads of sq are done
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t c = ((uint32_t)codes[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-      sq[(lk + j) * kTileRows + lr] = (double)e4m3_to_f32(c) * (double)scale;
+    for (int j = 0; j < CB; ++j) {
+      const uint4 q4 = codes[j >> 4];
+      const uint32_t wd = (j & 15) < 4 ? q4.x : (j & 15) < 8 ? q4.y : (j & 15) < 12 ? q4.z : q4.w;
+      const uint32_t c = (wd >> (8 * (j & 3))) & 0xFFu;
+      sq[(lk + j) * TR + lr] = (double)e4m3_to_f32(c) * (double)scale;
     }
     __syncthreads();
     load(tile + gridDim.x, codes, scale);
-    double acc[8][4];
+    double acc[RPT][4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+    for (int r = 0; r < RPT; ++r)
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
     // the LDS reads of step k + 1 are issued before the FMAs of step k
-    auto rd = [&](int k, float4& wv, double2 (&qv)[4]) {
+    auto rd = [&](int k, float4& wv, double2 (&qv)[RPT / 2]) {
       wv = *(const float4*)(sw + k * kIdxDim + 4 * tx);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) qv[r] = *(const double2*)(sq + k * kTileRows + 8 * ty + 2 * r);
+      for (int r = 0; r < RPT / 2; ++r) qv[r] = *(const double2*)(sq + k * TR + RPT * ty + 2 * r);
     };
-    auto fmas = [&](const float4& wv, const double2 (&qv)[4]) {
+    auto fmas = [&](const float4& wv, const double2 (&qv)[RPT / 2]) {
       const double w4[4] = {(double)wv.x, (double)wv.y, (double)wv.z, (double)wv.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RPT / 2; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           acc[2 * r][c] = fma(qv[r].x, w4[c], acc[2 * r][c]);
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(256, 1) void fold_tile_kernel(const uint8_t* __rest
         }
     };
     float4 wa, wb;
-    double2 qa[4], qb[4];
+    double2 qa[RPT / 2], qb[RPT / 2];
     rd(0, wa, qa);
     for (int k = 0; k < kIdxDim; k += 2) {
       rd(k + 1, wb, qb);
@@ -243,8 +250,8 @@ __global__ __launch_bounds__(256, 1) void fold_tile_kernel(const uint8_t* __rest
       fmas(wb, qb);
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t t = tile * kTileRows + 8 * ty + r;
+    for (int r = 0; r < RPT; ++r) {
+      const int64_t t = tile * TR + RPT * ty + r;
       double m = fmax(fmax(fabs(acc[r][0]), fabs(acc[r][1])), fmax(fabs(acc[r][2]), fabs(acc[r][3])));
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void fold_tile_kernel(const uint8_t* __rest
     }
   }
 }
-constexpr size_t kFoldTileLds = (size_t)kIdxDim * kIdxDim * 4 + (size_t)kIdxDim * kTileRows * 8;
+constexpr size_t fold_tile_lds(int tr) { return (size_t)kIdxDim * kIdxDim * 4 + (size_t)kIdxDim * tr * 8; }
 
 template <int R>
 static void launch_fold_rows(const void* q_in, const float* q_scale, bool fp8_in, const void* w, bool w_bf16,
@@ -280,9 +287,6 @@ hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, cons
   // 4-byte packed stores
   const bool tile_ok = ((uintptr_t)q_in % 32 == 0) && ((uintptr_t)w % 16 == 0) && ((uintptr_t)q_out % 4 == 0);
   if (T >= 8192 && fp8_in && w_bf16 && tile_ok) {
-    static std::atomic<uint64_t> lds_done{0};
-    const hipError_t e = set_lds_limit_once((const void*)fold_tile_kernel, (int)kFoldTileLds, lds_done);
-    if (e != hipSuccess) return e;
     int cus = 256;
     {
       int dev = 0;
@@ -290,9 +294,22 @@ hipError_t launch_fold(const void* q_in, const float* q_scale, bool fp8_in, cons
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = 256;
     }
-    const int64_t tiles = (T + kTileRows - 1) / kTileRows;
-    fold_tile_kernel<<<(unsigned)(tiles < cus ? tiles : cus), 256, kFoldTileLds, st>>>(
-        (const uint8_t*)q_in, q_scale, (const uint16_t*)w, T, (uint8_t*)q_out, s_out);
+    // 64-row tiles once they cover every CU, else 32-row tiles (twice the blocks)
+    const int64_t tiles64 = (T + 63) / 64;
+    if (tiles64 >= cus) {
+      static std::atomic<uint64_t> lds_done{0};
+      const hipError_t e = set_lds_limit_once((const void*)fold_tile_kernel<64>, (int)fold_tile_lds(64), lds_done);
+      if (e != hipSuccess) return e;
+      fold_tile_kernel<64><<<(unsigned)cus, 256, fold_tile_lds(64), st>>>(
+          (const uint8_t*)q_in, q_scale, (const uint16_t*)w, T, (uint8_t*)q_out, s_out);
+    } else {
+      static std::atomic<uint64_t> lds_done{0};
+      const hipError_t e = set_lds_limit_once((const void*)fold_tile_kernel<32>, (int)fold_tile_lds(32), lds_done);
+      if (e != hipSuccess) return e;
+      const int64_t tiles = (T + 31) / 32;
+      fold_tile_kernel<32><<<(unsigned)(tiles < cus ? tiles : cus), 256, fold_tile_lds(32), st>>>(
+          (const uint8_t*)q_in, q_scale, (const uint16_t*)w, T, (uint8_t*)q_out, s_out);
+    }
   } else if (T >= 8192)
     launch_fold_rows<32>(q_in, q_scale, fp8_in, w, w_bf16, T, q_out, s_out, st);
   else {
