@@ -17,7 +17,7 @@ the kernel runs on; its roofline uses algorithmic FLOPs (or bytes) only, and
 is stated against both the published peak and the peak measured in the same
 run by the probe library (an MFMA issue loop and a streaming HBM read).  GPU
 clocks and power are read before the timed region, during (sampled while
-about 4 s of further, untimed steps of the same workload run right after
+about 5 s of further, untimed steps of the same workload run right after
 it) and after.  The 8K and 32K prefills are timed as extra
 lines; decode is timed warm (one cache set) and
 cold (four cache sets in rotation, 24 GB, far past the 256 MB last-level
@@ -158,16 +158,20 @@ def clock_summary(flat):
 
 
 class ClockSampler:
-    """Reads the clocks once on a helper thread while the GPU runs queued
-    work (the host is blocked in a synchronisation meanwhile; the caller
-    queues enough work to outlast the tool's start-up)."""
+    """Reads the clocks once on a helper thread, `delay` seconds after it
+    starts, while the GPU runs queued work (the caller queues enough work to
+    outlast the delay and the tool's start-up).  The delay also keeps the
+    read apart from an earlier one: a read within about a second of the
+    previous one can return the same cached metrics."""
 
-    def __init__(self):
+    def __init__(self, delay=1.5):
         import threading
         self.result = None
+        self.delay = delay
         self.t = threading.Thread(target=self._run, daemon=True)
 
     def _run(self):
+        time.sleep(self.delay)
         self.result = gpu_clocks()
 
     def start(self):
@@ -801,11 +805,13 @@ def time_prefill(B, torch, dev, spec, x, steps, warmup, peaks, dyn_theta=None, d
     dt = (time.perf_counter() - t0) / steps
     clocks_during = None
     if keep:
-        # the clock tool takes about a second to start: read it while further
-        # untimed steps of the same workload keep the GPU busy for ~4 s
-        for _ in range(max(1, int(math.ceil(4.0 / dt)))):
-            step()
+        # the sampler reads the clocks 1.5 s after it starts (the tool itself
+        # takes about a second); meanwhile ~5 s of further untimed steps of
+        # the same workload keep the GPU busy (the launches may block once the
+        # queue is full, so the sampler starts first)
         sampler = ClockSampler().start()
+        for _ in range(max(1, int(math.ceil(5.0 / dt)))):
+            step()
         torch.cuda.synchronize()
         clocks_during = sampler.join()
     log(f"{spec.name}: prefill {dt * 1e3:.2f} ms/step, {L / dt:.4g} tokens/s")
