@@ -59,7 +59,14 @@ UNIT_MLA = gen.PREFILL_32K.with_(name="unit_L1500_mla", L=1500, topk=300, qkv_un
 
 # ------------------------------------------------------------------ fold ---
 
-@pytest.mark.parametrize("spec", [gen.TINY_F32, gen.PREFILL_8K, SMALL_MLA], ids=lambda s: s.name)
+# the tiled fold: 32-row tiles with a ragged last tile (fewer tiles than
+# CUs), and 64-row tiles outnumbering the grid with a ragged last tile
+FOLD_T32 = gen.PREFILL_8K.with_(name="fold_L8232", L=8232)
+FOLD_T64 = gen.PREFILL_8K.with_(name="fold_L16424", L=16424)
+
+
+@pytest.mark.parametrize("spec", [gen.TINY_F32, gen.PREFILL_8K, SMALL_MLA, FOLD_T32, FOLD_T64],
+                         ids=lambda s: s.name)
 def test_fold(dev, spec):
     say("fold", spec.name)
     x = gen.make_prefill(spec, seed=1, device=dev)
