@@ -150,6 +150,8 @@ ATTN_CASES = [
     ("f32_h4_d64", gen.TINY_F32.with_(L=300), 64),
     ("bf16_h16_d128", gen.PREFILL_8K.with_(L=3000), 2048),
     ("bf16_h16_k4096", gen.PREFILL_8K.with_(L=5000), 4096),
+    ("bf16_h16_k5", gen.PREFILL_8K.with_(L=300), 5),                 # one partial 16-key tile
+    ("bf16_mla_k5", gen.PREFILL_32K.with_(L=300), 5),                 # one partial 32-key tile
     ("bf16_mla", gen.PREFILL_32K.with_(L=2500), 2048),
     ("bf16_mla_unit", gen.PREFILL_32K.with_(L=2500, qkv_unit=True), 700),
     ("bf16_mla_k4096", gen.PREFILL_32K.with_(L=5000), 4096),      # the largest k
