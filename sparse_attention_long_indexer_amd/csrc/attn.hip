@@ -865,9 +865,28 @@ __global__ __launch_bounds__(512, 1) void attn_mla_kernel(AttnArgs a, const int6
   // slot 2j: group 0 S^T + softmax of tile j, group 1 PV of tile j-1 (and
   // the gather of tile j+1); slot 2j+1: group 1 S^T + softmax of tile j,
   // group 0 PV of tile j-1.  Both groups pass the same 2 ntiles + 2 barriers.
+  // The block that most likely runs next on this CU, query t + a.ahead
+  // (a.ahead = the chip's CU count: blocks are dealt round-robin, so it is on
+  // the same XCD), finds its index row in the cache: one 4-byte
+  // direct-to-LDS copy per 128-byte line of the row into a dummy slot.  One
+  // wave of group 0 issues them; its loop has no other global loads, so
+  // nothing waits for them.  Its index row is the head of that block's
+  // dependent chain (index row, first gather, first S^T).
+  auto prefetch_next_index_row = [&]() {
+    const int64_t tn = t + a.ahead;
+    if (a.ahead <= 0 || tn >= a.T || w != 0) return;
+    lds_char* dummy = (lds_char*)(smem + kMlaFixedLds) + a.k * 4;
+    const int lines = (int)((a.k + 31) / 32);   // 32 entries per line; each copy reads the line's first entry
+    for (int l0 = 0; l0 < lines; l0 += 64) {
+      const int ln = min(l0 + lane, lines - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(a.idx + tn * a.k + 32 * ln),
+                                       (__attribute__((address_space(3))) void*)dummy, 4, 0, 0);
+    }
+  };
   if (G == 0) {
     __syncthreads();
     for (int jj = 0; jj <= ntiles; ++jj) {
+      if (jj == 2) prefetch_next_index_row();
       if (jj < ntiles) qk_softmax(jj);
       lds_barrier();
       if (jj >= 1) pv(jj - 1);
@@ -1177,9 +1196,10 @@ static hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
 }
 
 static hipError_t launch_mla(const AttnArgs& a, const int64_t* seq_off, hipStream_t st) {
-  constexpr size_t lds_max = kMlaFixedLds + (size_t)DSA_MAX_TOPK * 4;
-  static_assert(lds_max <= kAttnLdsLimit, "three tiles, P^T and the index row fit in LDS");
-  const size_t lds = kMlaFixedLds + (size_t)a.k * 4;
+  // + 256 bytes: the dummy slot of the index-row prefetch
+  constexpr size_t lds_max = kMlaFixedLds + (size_t)DSA_MAX_TOPK * 4 + 256;
+  static_assert(lds_max <= kAttnLdsLimit, "three tiles, P^T, the index row and the dummy slot fit in LDS");
+  const size_t lds = kMlaFixedLds + (size_t)a.k * 4 + 256;
   static std::atomic<uint64_t> attr_done{0};
   hipError_t ea = set_lds_limit_once((const void*)attn_mla_kernel, (int)lds_max, attr_done);
   if (ea != hipSuccess) return ea;
@@ -1193,6 +1213,15 @@ hipError_t launch_attn(const AttnArgs& a_in, bool f32, void* ws, size_t ws_bytes
   if (a_in.T <= 0) return hipSuccess;
   AttnArgs a = a_in;
   a.splits = attn_splits(f32, a.T, a.k);
+  // queries ahead whose index row a block prefetches (one block per query
+  // and CU): the device's CU count
+  a.ahead = 0;
+  if (a.splits == 1) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+      a.ahead = ncu;
+  }
   if (a.splits > 1) {
     if (!ws || ws_bytes < attn_workspace_bytes(f32, a.T, a.H, a.Dv, a.k)) return hipErrorInvalidValue;
     const size_t rows = (size_t)a.T * a.splits * a.H;

@@ -131,6 +131,7 @@ struct AttnArgs {
   uint16_t* part_o;     // [T][splits][H][Dv] fp16: unnormalised partial output / its slice scale
   float* part_ml;       // [T][splits][H][2] running max (log2) and sum
   float* part_sc;       // [T][splits][H][Dv/64] slice scales: max |partial| over 64 value columns
+  int64_t ahead;        // MLA kernel: a block prefetches the index row of query t + ahead (0: none)
 };
 bool attn_supported(bool f32, int64_t H, int64_t Dk, int64_t Dv, bool sep_v, int64_t k);
 size_t attn_workspace_bytes(bool f32, int64_t T, int64_t H, int64_t Dv, int64_t k);
